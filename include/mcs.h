@@ -1,0 +1,175 @@
+/*
+ * mcs.h — C ABI of the MC-Sparse attention hot path on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (web pages on "MC-Sparse: Analyzing and Bridging the Dense-Sparse
+ * Attention Gap in Diffusion Transformers"; the onedev.kr summary, sections
+ * "what is different" and "how it is used", and the ai-feeds.com summary,
+ * sections "method" and "integration interface"):
+ *
+ *   anchor step  tau:  O_full = dense attention (the layer output)
+ *                      G     = tile-aligned query groups (Fast PDDP)
+ *                      S     = per-group KV token indices chosen by exact
+ *                              attention probabilities (two passes)
+ *                      R     = O_full - SparseAttn(Q, K, V; G, S)
+ *   reuse step   t:    O_t   = SparseAttn(Q_t, K_t, V_t; G, S) + R
+ *
+ * Calls, in the order a caller uses them:
+ *   anchor: mcs_group -> mcs_anchor_select -> mcs_residual
+ *   reuse : mcs_sparse_attn
+ *   mcs_dense_attn is the in-house dense kernel (anchor pass 1, and the
+ *   denominator of the sparse kernel's speed-up).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Tensors are device pointers to contiguous row-major arrays.  bf16 values are
+ * passed as uint16_t bit patterns.  Shapes use the dims struct:
+ *   Q, K, V, O, O_full, R : bf16  [batch, heads, n_pad, head_dim]
+ *   lse                   : fp32  [batch, heads, n_pad]   (natural log)
+ *   perm                  : int32 [batch, heads, n_pad]   group g = perm[g*C .. g*C+C-1]
+ *   kv_idx                : int32 [batch, heads, n_pad/C, topk], ascending per group
+ * Rows n_valid .. n_pad-1 are padding: the caller zero-fills them in Q, K, V;
+ * padded keys never take part in a softmax and are never selected; padded
+ * query rows take part in grouping as all-zero rows and get O = R = 0, lse = 0.
+ * Supported: head_dim in {64, 128}; group_size C in {64, 128}; n_pad a
+ * multiple of C; 1 <= n_valid <= n_pad <= 2^24; 1 <= topk <= n_valid;
+ * batch*heads*n_pad*head_dim < 2^40.  Every pointer must be 16-byte aligned.
+ *
+ * Ownership: the caller allocates every buffer, workspaces included.  The
+ * library never allocates, frees or keeps device memory and holds no state
+ * between calls; the metadata (perm, kv_idx, R) is ordinary caller memory that
+ * may be cached, offloaded to the host or reloaded between steps.
+ *
+ * Asynchrony: every call only enqueues work on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns.  Outputs are valid once the stream reaches
+ * that point.  Calls on one stream run in order.
+ *
+ * Errors: arguments are checked before anything is enqueued.  On a bad
+ * argument the call returns MCS_ERR_INVALID_ARG / MCS_ERR_UNSUPPORTED /
+ * MCS_ERR_WORKSPACE, enqueues nothing, leaves every output untouched and
+ * records a message for mcs_last_error() (per calling thread).  A failed kernel
+ * launch returns MCS_ERR_HIP.  Faults inside kernels surface at the caller's
+ * next synchronisation.
+ *
+ * Determinism: no floating-point atomics are used; for identical inputs on the
+ * same device every output is bitwise identical from run to run.
+ */
+#ifndef MCS_H
+#define MCS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MCS_ABI_VERSION 1
+
+typedef enum {
+  MCS_OK = 0,
+  MCS_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad scale   */
+  MCS_ERR_UNSUPPORTED = 2, /* shape outside the supported set above         */
+  MCS_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than needed  */
+  MCS_ERR_HIP = 4          /* a HIP launch or runtime call failed            */
+} mcs_status;
+
+typedef struct {
+  int32_t batch;      /* B                                   */
+  int32_t heads;      /* H                                   */
+  int32_t n_valid;    /* N, real tokens                      */
+  int32_t n_pad;      /* N rounded up to a multiple of C     */
+  int32_t head_dim;   /* d                                   */
+  int32_t group_size; /* C, the query tile = group size      */
+} mcs_dims;
+
+int32_t mcs_abi_version(void);
+const char* mcs_status_string(int32_t status);
+/* Message of this thread's last failed call ("" if none). */
+const char* mcs_last_error(void);
+
+/*
+ * mcs_group — Fast PDDP grouping (onedev.kr summary, "how it is used",
+ * component 2).  Builds, per (batch, head), a binary tree of C-aligned median
+ * splits: a node of m groups is projected on the principal direction of its
+ * centred query rows (power iteration from v0 = 1/sqrt(d), `power_iters`
+ * steps, sign fixed so the largest-magnitude component is positive, lowest
+ * index on ties) and its members ordered by (projection, token index); the
+ * first floor(m/2)*C go to the left child, the rest to the right.  All nodes of
+ * one depth, across all heads, are processed by the same launches and only the
+ * index array moves between depths.  Arithmetic is fp64 on the bf16 inputs.
+ *   q          : bf16 [B,H,n_pad,d], the anchor step's queries (padding rows 0)
+ *   power_iters: 0 .. 1000 (20 in the method's configurations)
+ *   max_levels : -1 = all ceil(log2(n_pad/C)) depths; 0..L = stop after that
+ *                many depths (partial trees, for testing)
+ *   perm       : out, int32 [B,H,n_pad]; group g = perm[g*C .. g*C+C-1], members
+ *                ascending; groups numbered left to right in the tree.
+ *   workspace  : at least mcs_group_workspace_bytes(dims) bytes, 256-aligned.
+ */
+size_t mcs_group_workspace_bytes(const mcs_dims* dims);
+int32_t mcs_group(const mcs_dims* dims, const uint16_t* q, int32_t power_iters,
+                  int32_t max_levels, int32_t* perm, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * mcs_anchor_select — the two-pass exact selection (onedev.kr summary, "how it
+ * is used", components 1 and 3): pass 1 is dense attention writing O_full and
+ * lse; pass 2 recomputes the logits of every group's members and scores each
+ * valid key j by a_g[j] = sum over valid members i of exp(s_ij - lse_i), the
+ * group's aggregated exact attention probability; the `topk` largest scores
+ * (ties to the lower key index) are written ascending to kv_idx.
+ *   q, k, v : bf16 [B,H,n_pad,d] at the anchor step
+ *   perm    : from mcs_group
+ *   scale   : softmax scale (1/sqrt(d) in the method), finite and > 0
+ *   o_full  : out, bf16 [B,H,n_pad,d]; lse: out, fp32 [B,H,n_pad]
+ *   kv_idx  : out, int32 [B,H,G,topk]
+ *   workspace: mcs_anchor_select_workspace_bytes(dims, topk) lets all heads
+ *           run at once; any size >= mcs_anchor_select_min_workspace_bytes
+ *           works (heads are then processed in chunks).
+ */
+size_t mcs_anchor_select_workspace_bytes(const mcs_dims* dims, int32_t topk);
+size_t mcs_anchor_select_min_workspace_bytes(const mcs_dims* dims, int32_t topk);
+int32_t mcs_anchor_select(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const int32_t* perm, int32_t topk, float scale,
+                          uint16_t* o_full, float* lse, int32_t* kv_idx, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * mcs_residual — R = O_full - SparseAttn(Q, K, V; perm, kv_idx) at the anchor
+ * (onedev.kr summary, "what is different").  The sparse softmax is normalised
+ * over each group's own index set.  Padded rows of R are 0.
+ *   o_full : in, bf16 [B,H,n_pad,d];  r : out, bf16 [B,H,n_pad,d]
+ */
+int32_t mcs_residual(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                     int32_t topk, float scale, const uint16_t* o_full, uint16_t* r,
+                     void* stream);
+
+/*
+ * mcs_sparse_attn — the reuse step O_t = SparseAttn(Q_t, K_t, V_t; G, S) + R
+ * (onedev.kr summary, "what is different"; "how it is used", component 1: K
+ * and V rows are gathered on line from the cached indices).  Each group's C
+ * queries attend to exactly its topk keys kv_idx[g]; the softmax is normalised
+ * over that set; R (nullable: no residual) is added in the epilogue; the result
+ * is written in token order.  Padded rows of O are 0.
+ *   o : out, bf16 [B,H,n_pad,d]; must not alias q, k, v or r.
+ */
+int32_t mcs_sparse_attn(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                        int32_t topk, float scale, const uint16_t* r, uint16_t* o,
+                        void* stream);
+
+/*
+ * mcs_dense_attn — dense softmax attention over the n_valid keys, with the
+ * per-row log-sum-exp (nullable).  The dense baseline of the onedev.kr
+ * summary ("assumptions and limits") and anchor pass 1.
+ *   o : out, bf16 [B,H,n_pad,d];  lse : out, fp32 [B,H,n_pad] or NULL
+ */
+int32_t mcs_dense_attn(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, float scale, uint16_t* o, float* lse,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MCS_H */

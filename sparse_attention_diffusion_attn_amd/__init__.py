@@ -1,0 +1,240 @@
+"""MC-Sparse attention hot path on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C-ABI library libmcs.so (include/mcs.h).  The
+functions here only check and marshal arguments; every step of the path runs
+in the library's HIP kernels.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if libmcs.so is missing or fails to load, every
+call raises.
+
+Anchor step:  perm = group(q, ...);  o_full, lse, kv_idx = anchor_select(...);
+              r = residual(...)
+Reuse step:   o = sparse_attn(q_t, k_t, v_t, perm, kv_idx, r, ...)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmcs.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mcs.h")
+
+MCS_OK, MCS_ERR_INVALID_ARG, MCS_ERR_UNSUPPORTED, MCS_ERR_WORKSPACE, MCS_ERR_HIP = range(5)
+
+
+class MCSError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {message} (status {status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("n_valid", ctypes.c_int32),
+                ("n_pad", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+_DP = ctypes.POINTER(Dims)
+
+_SIGNATURES = {
+    "mcs_abi_version": (_I, []),
+    "mcs_status_string": (ctypes.c_char_p, [_I]),
+    "mcs_last_error": (ctypes.c_char_p, []),
+    "mcs_group_workspace_bytes": (_SZ, [_DP]),
+    "mcs_group": (_I, [_DP, _P, _I, _I, _P, _P, _SZ, _P]),
+    "mcs_anchor_select_workspace_bytes": (_SZ, [_DP, _I]),
+    "mcs_anchor_select_min_workspace_bytes": (_SZ, [_DP, _I]),
+    "mcs_anchor_select": (_I, [_DP, _P, _P, _P, _P, _I, _F, _P, _P, _P, _P, _SZ, _P]),
+    "mcs_residual": (_I, [_DP, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P]),
+    "mcs_sparse_attn": (_I, [_DP, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P]),
+    "mcs_dense_attn": (_I, [_DP, _P, _P, _P, _F, _P, _P, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmcs.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_attention_diffusion_attn_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def header_functions() -> list:
+    """Names of the functions include/mcs.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"\b(mcs_[a-z_]+)\s*\(", text)))
+
+
+def _check(status: int, where: str) -> None:
+    if status != MCS_OK:
+        msg = lib().mcs_last_error().decode()
+        raise MCSError(status, where, msg)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_dims(batch, heads, n_valid, n_pad, head_dim, group_size) -> Dims:
+    return Dims(batch, heads, n_valid, n_pad, head_dim, group_size)
+
+
+def _dims_of(q: torch.Tensor, n_valid: int, group_size: int) -> Dims:
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, n_pad, head_dim]")
+    b, h, n_pad, d = q.shape
+    return Dims(b, h, n_valid, n_pad, d, group_size)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+def group_workspace_bytes(dims: Dims) -> int:
+    return int(lib().mcs_group_workspace_bytes(ctypes.byref(dims)))
+
+
+def anchor_select_workspace_bytes(dims: Dims, topk: int, minimum: bool = False) -> int:
+    fn = lib().mcs_anchor_select_min_workspace_bytes if minimum else lib().mcs_anchor_select_workspace_bytes
+    return int(fn(ctypes.byref(dims), topk))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is None:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+def group(q: torch.Tensor, n_valid: int, group_size: int, power_iters: int = 20,
+          max_levels: int = -1, perm: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Fast PDDP grouping -> perm int32 [B, H, n_pad] (mcs_group)."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    if perm is None:
+        perm = torch.empty((b, h, n_pad), dtype=torch.int32, device=q.device)
+    ws = _workspace(group_workspace_bytes(dims), q.device, workspace)
+    st = lib().mcs_group(ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), power_iters,
+                         max_levels, _need(perm, "perm", torch.int32, (b, h, n_pad)),
+                         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "mcs_group")
+    return perm
+
+
+def anchor_select(q, k, v, perm, n_valid: int, group_size: int, topk: int,
+                  scale: Optional[float] = None, o_full=None, lse=None, kv_idx=None,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """Two-pass exact selection -> (o_full, lse, kv_idx) (mcs_anchor_select)."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    G = n_pad // group_size
+    scale = default_scale(d) if scale is None else scale
+    if o_full is None:
+        o_full = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((b, h, n_pad), dtype=torch.float32, device=q.device)
+    if kv_idx is None:
+        kv_idx = torch.empty((b, h, G, topk), dtype=torch.int32, device=q.device)
+    ws = _workspace(anchor_select_workspace_bytes(dims, topk), q.device, workspace)
+    st = lib().mcs_anchor_select(
+        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
+        _need(v, "v", torch.bfloat16, q.shape), _need(perm, "perm", torch.int32, (b, h, n_pad)),
+        topk, scale, _need(o_full, "o_full", torch.bfloat16, q.shape),
+        _need(lse, "lse", torch.float32, (b, h, n_pad)),
+        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "mcs_anchor_select")
+    return o_full, lse, kv_idx
+
+
+def residual(q, k, v, perm, kv_idx, o_full, n_valid: int, group_size: int,
+             scale: Optional[float] = None, r=None, stream=None) -> torch.Tensor:
+    """R = O_full - SparseAttn(Q, K, V; perm, kv_idx) (mcs_residual)."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    G = n_pad // group_size
+    topk = kv_idx.shape[-1]
+    scale = default_scale(d) if scale is None else scale
+    if r is None:
+        r = torch.empty_like(q)
+    st = lib().mcs_residual(
+        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
+        _need(v, "v", torch.bfloat16, q.shape), _need(perm, "perm", torch.int32, (b, h, n_pad)),
+        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)), topk, scale,
+        _need(o_full, "o_full", torch.bfloat16, q.shape), _need(r, "r", torch.bfloat16, q.shape),
+        _stream(stream))
+    _check(st, "mcs_residual")
+    return r
+
+
+def sparse_attn(q, k, v, perm, kv_idx, r, n_valid: int, group_size: int,
+                scale: Optional[float] = None, o=None, stream=None) -> torch.Tensor:
+    """Reuse step O = SparseAttn(Q, K, V; perm, kv_idx) + R (mcs_sparse_attn).
+    `r` may be None (no residual)."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    G = n_pad // group_size
+    topk = kv_idx.shape[-1]
+    scale = default_scale(d) if scale is None else scale
+    if o is None:
+        o = torch.empty_like(q)
+    rp = None if r is None else _need(r, "r", torch.bfloat16, q.shape)
+    st = lib().mcs_sparse_attn(
+        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
+        _need(v, "v", torch.bfloat16, q.shape), _need(perm, "perm", torch.int32, (b, h, n_pad)),
+        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)), topk, scale, rp,
+        _need(o, "o", torch.bfloat16, q.shape), _stream(stream))
+    _check(st, "mcs_sparse_attn")
+    return o
+
+
+def dense_attn(q, k, v, n_valid: int, group_size: int = 128, scale: Optional[float] = None,
+               o=None, lse=None, want_lse: bool = True, stream=None):
+    """Dense attention -> (o, lse) (mcs_dense_attn)."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    scale = default_scale(d) if scale is None else scale
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((b, h, n_pad), dtype=torch.float32, device=q.device)
+    lp = None if lse is None else _need(lse, "lse", torch.float32, (b, h, n_pad))
+    st = lib().mcs_dense_attn(
+        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
+        _need(v, "v", torch.bfloat16, q.shape), scale, _need(o, "o", torch.bfloat16, q.shape), lp,
+        _stream(stream))
+    _check(st, "mcs_dense_attn")
+    return o, lse

@@ -1,0 +1,53 @@
+"""Build libmcs.so (the C-ABI library of the hot path) for gfx950 with hipcc.
+
+Usage: python -m sparse_attention_diffusion_attn_amd.build
+Objects go to <package>/_build/, the library to <package>/libmcs.so.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT = os.path.join(PKG, "libmcs.so")
+SOURCES = ["attn.hip", "select.hip", "pddp.hip", "mcs_api.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU forms are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
+]
+
+
+def _compile(src: str, obj: str) -> None:
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+
+
+def build(verbose: bool = False) -> str:
+    bdir = os.path.join(PKG, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        list(ex.map(_compile, SOURCES, objs))
+    tmp = OUT + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, OUT)
+    if verbose:
+        print(f"built {OUT}")
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

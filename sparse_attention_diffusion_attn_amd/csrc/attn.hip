@@ -1,0 +1,274 @@
+// Dense, token-sparse and residual attention on gfx950 (one kernel template).
+//
+// The token-sparse mode is the reuse step of MC-Sparse (onedev.kr summary,
+// "what is different": O_t = SparseAttn(Q_t, K_t, V_t; G, S) + R; "how it is
+// used", component 1: K/V rows are gathered on line from the cached indices).
+// The dense mode is the dense baseline and anchor pass 1; the residual mode
+// writes R = O_full - SparseAttn(...) at the anchor.
+//
+// One workgroup per (head, query group): C/32 wavefronts, each owning 32 query
+// rows.  Key/value tiles of 64 rows are gathered by index with 16-byte
+// global->LDS copies into a double-buffered LDS tile (column planes, chunks
+// permuted per row against bank conflicts); the loads of
+// tile t+1 (and the indices of tile t+2) are in flight while tile t is
+// consumed.  Both contractions run on v_mfma_f32_32x32x16_bf16:
+//   S^T = K_tile . Q^T   (A = gathered K rows from LDS, B = Q held in VGPRs)
+//   O^T += V_tile^T . P^T (A = V via transposing LDS reads, B = P from the S^T
+//                          accumulators, converted to bf16)
+// so every lane owns one query row for the whole online softmax (fp32, exp2
+// with the scale folded in); the only cross-lane step is one max exchange.
+// The dense mode runs the very same code with contiguous key rows, so the
+// sparse/dense time ratio measures the cost of gathering alone.
+#include "mcs_common.h"
+#include "mcs_internal.h"
+
+namespace mcs {
+
+template <int D, int C, int MODE>
+__global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
+  constexpr int NW = C / 32;            // wavefronts, 32 query rows each
+  constexpr int KT = 64;                // keys per tile
+  constexpr int NPL = D / 32;           // column planes per tile (4 KiB each)
+  constexpr int TILE = NPL * 4096;      // bytes per matrix tile
+  constexpr int IPM = TILE / 1024;      // 1 KiB copy instructions per matrix tile
+  constexpr int IPW = IPM / NW;         // ... per wavefront
+  constexpr int KS = D / 16;            // k-steps of the QK^T product
+  static_assert(IPW >= 1 && IPM % NW == 0, "tile split");
+
+  __shared__ __attribute__((aligned(1024))) char lds[4 * TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int ql = lane & 31;
+  const int h = lane >> 5;
+
+  const int G = p.groups;
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bh = work / G;
+  const int g = work - (int)(bh * G);
+  const size_t mat = (size_t)bh * p.n_pad * D;
+  const uint16_t* Qb = p.q + mat;
+  const uint16_t* Kb = p.k + mat;
+  const uint16_t* Vb = p.v + mat;
+
+  // ---- query rows of this lane (B operand of S^T, resident in VGPRs) ----
+  const int qpos = g * C + 32 * w + ql;
+  const int qrow = (MODE == ATTN_DENSE) ? qpos : p.perm[(size_t)bh * p.n_pad + qpos];
+  bf16x8 qreg[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    qreg[kk] = *(const bf16x8*)(Qb + (size_t)qrow * D + 16 * kk + 8 * h);
+
+  const int nk = (MODE == ATTN_DENSE) ? p.n_valid : p.topk;
+  const int ntiles = (nk + KT - 1) / KT;
+  const int32_t* idxrow =
+      (MODE == ATTN_DENSE) ? nullptr : p.kv_idx + ((size_t)bh * G + g) * p.topk;
+
+  // ---- gather geometry ----
+  // Copy instruction `ins` fills plane ins/4, tile rows 16*(ins%4) .. +15;
+  // lane l writes row 16*(ins%4) + l/4, physical chunk l%4, i.e. logical
+  // chunk (l%4) ^ ((l/16)%4) of that plane: columns 32*(ins/4) + 8*chunk.
+  const int grow = lane >> 2;
+  const int gcol = 8 * ((lane ^ (lane >> 4)) & 3);
+  int tok[IPW];
+  auto fetch_idx = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int ins = w * IPW + i;
+      int pos = t * KT + 16 * (ins & 3) + grow;
+      if (MODE == ATTN_DENSE) {
+        tok[i] = pos;
+      } else {
+        pos = pos < nk ? pos : nk - 1;
+        tok[i] = idxrow[pos];
+      }
+    }
+  };
+  auto issue = [&](int buf) {
+    char* kdst = lds + buf * 2 * TILE;
+    char* vdst = kdst + TILE;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int ins = w * IPW + i;
+      const size_t off = (size_t)tok[i] * D + 32 * (ins >> 2) + gcol;
+      gather16(Kb + off, kdst + ins * 1024);
+      gather16(Vb + off, vdst + ins * 1024);
+    }
+  };
+
+  // ---- LDS read geometry (base + compile-time offsets) ----
+  // QK^T operand: rows ql (+32), 16-byte chunk 2*kk+h = plane kk/2, in-plane
+  // chunk 2*(kk%2)+h.
+  const int sq = (ql >> 2) & 3;
+  const int koff_e = ql * 64 + ((h ^ sq) << 4);
+  const int koff_o = ql * 64 + (((2 + h) ^ sq) << 4);
+  // PV operand: transposing reads of rows 16u + 4h + jj/4 (and +8) at plane
+  // columns 16*(qq%2) + 4*(jj%4).
+  const int jj = lane & 15, qq = lane >> 4;
+  const int vrow = 4 * h + (jj >> 2);
+  const int vchunk = 2 * (qq & 1) + ((jj & 3) >> 1);
+  const int vhalf = 8 * (jj & 1);
+  const int voff_a = vrow * 64 + ((vchunk ^ h) << 4) + vhalf;
+  const int voff_b = (vrow + 8) * 64 + ((vchunk ^ h ^ 2) << 4) + vhalf;
+
+  f32x16 o[NPL];
+#pragma unroll
+  for (int T = 0; T < NPL; ++T)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[T][j] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
+  const float c2 = p.scale * kLog2e;
+
+  fetch_idx(0);
+  issue(0);
+  if (ntiles > 1) fetch_idx(1);
+
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vm0();
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      issue((t + 1) & 1);
+      if (t + 2 < ntiles) fetch_idx(t + 2);
+    }
+    const char* kbuf = lds + (t & 1) * 2 * TILE;
+    const char* vbuf = kbuf + TILE;
+
+    // S^T = K . Q^T for the 64 keys of this tile (two 32-key blocks)
+    f32x16 s0, s1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) { s0[j] = 0.f; s1[j] = 0.f; }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const char* kp = kbuf + ((kk & 1) ? koff_o : koff_e) + (kk >> 1) * 4096;
+      const bf16x8 a0 = *(const bf16x8*)(kp);
+      const bf16x8 a1 = *(const bf16x8*)(kp + 2048);
+      s0 = mfma32(a0, qreg[kk], s0);
+      s1 = mfma32(a1, qreg[kk], s1);
+    }
+
+    // mask keys past the end in the last tile
+    if ((t + 1) * KT > nk) {
+      const int lim = nk - t * KT;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = 8 * (j >> 2) + 4 * h + (j & 3);
+        if (key >= lim) s0[j] = -INFINITY;
+        if (key + 32 >= lim) s1[j] = -INFINITY;
+      }
+    }
+
+    // online softmax (this lane owns query ql; its partner lane ql+32 holds
+    // the other half of the tile's keys)
+    float mx = s0[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s0[j]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s1[j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(mrun, mx);
+    const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c2);
+    mrun = mnew;
+    const float mc = mnew * c2;
+    float ls = 0.f;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[j], c2, -mc));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[j], c2, -mc));
+      ls += e0 + e1;
+      pb[j >> 3][j & 7] = (__bf16)e0;
+      pb[2 + (j >> 3)][j & 7] = (__bf16)e1;
+    }
+    lrun = lrun * alpha + ls;
+#pragma unroll
+    for (int T = 0; T < NPL; ++T)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[T][j] *= alpha;
+
+    // O^T += V^T . P^T.  The transposing reads are issued from inline asm
+    // (with their wait inside the same block) so that the compiler does not
+    // make them wait for the global->LDS copies of the next tile, which write
+    // the other buffer.
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      i32x2 va[2 * NPL];
+      tr_read_planes<NPL>(va, vbuf + voff_a + u * 1024, vbuf + voff_b + u * 1024);
+#pragma unroll
+      for (int T = 0; T < NPL; ++T) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, (i32x4){va[2 * T][0], va[2 * T][1],
+                                                           va[2 * T + 1][0], va[2 * T + 1][1]});
+        o[T] = mfma32(a, pb[u], o[T]);
+      }
+    }
+  }
+
+  // ---- epilogue ----
+  const float lsum = lrun + __shfl_xor(lrun, 32);
+  const float inv = 1.f / lsum;
+  const bool valid = qrow < p.n_valid;
+  uint16_t* Ob = p.out + mat + (size_t)qrow * D;
+  const uint16_t* Ab = (p.aux != nullptr) ? p.aux + mat + (size_t)qrow * D : nullptr;
+#pragma unroll
+  for (int T = 0; T < NPL; ++T) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int col = 32 * T + 8 * gq + 4 * h;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = o[T][4 * gq + e] * inv;
+      if (MODE == ATTN_SPARSE && Ab != nullptr) {
+        const uint2 rv = *(const uint2*)(Ab + col);
+        x[0] += bf16_to_f32(rv.x & 0xffff);
+        x[1] += bf16_to_f32(rv.x >> 16);
+        x[2] += bf16_to_f32(rv.y & 0xffff);
+        x[3] += bf16_to_f32(rv.y >> 16);
+      } else if (MODE == ATTN_RESID) {
+        const uint2 ov = *(const uint2*)(Ab + col);
+        x[0] = bf16_to_f32(ov.x & 0xffff) - x[0];
+        x[1] = bf16_to_f32(ov.x >> 16) - x[1];
+        x[2] = bf16_to_f32(ov.y & 0xffff) - x[2];
+        x[3] = bf16_to_f32(ov.y >> 16) - x[3];
+      }
+      uint2 st;
+      if (valid) {
+        st.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+        st.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+      } else {
+        st.x = 0u;
+        st.y = 0u;
+      }
+      *(uint2*)(Ob + col) = st;
+    }
+  }
+  if (MODE == ATTN_DENSE && p.lse != nullptr && h == 0) {
+    p.lse[(size_t)bh * p.n_pad + qrow] = valid ? (mrun * p.scale + __logf(lsum)) : 0.f;
+  }
+}
+
+template <int D, int C, int MODE>
+static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
+  const int64_t items = p.bh * (int64_t)p.groups;
+  hipLaunchKernelGGL((attn_kernel<D, C, MODE>), dim3((unsigned)items), dim3(2 * C), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_mode(int d, int c, const AttnParams& p, hipStream_t s) {
+  if (d == 128 && c == 128) return launch_one<128, 128, MODE>(p, s);
+  if (d == 128 && c == 64) return launch_one<128, 64, MODE>(p, s);
+  if (d == 64 && c == 128) return launch_one<64, 128, MODE>(p, s);
+  if (d == 64 && c == 64) return launch_one<64, 64, MODE>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention(int mode, int head_dim, int group_size, const AttnParams& p,
+                            hipStream_t s) {
+  switch (mode) {
+    case ATTN_DENSE: return launch_mode<ATTN_DENSE>(head_dim, group_size, p, s);
+    case ATTN_SPARSE: return launch_mode<ATTN_SPARSE>(head_dim, group_size, p, s);
+    case ATTN_RESID: return launch_mode<ATTN_RESID>(head_dim, group_size, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mcs

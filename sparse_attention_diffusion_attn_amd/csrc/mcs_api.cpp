@@ -1,0 +1,334 @@
+// C ABI of the MC-Sparse hot path: argument checks, workspace carving and
+// kernel launches.  Every check runs before anything is enqueued, so a bad
+// call leaves outputs untouched and the stream unchanged; the library keeps no
+// device memory and no state between calls.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mcs.h"
+#include "mcs_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return MCS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int levels_for(int groups) {
+  int l = 0;
+  while ((1 << l) < groups) ++l;
+  return l;
+}
+
+// Shape checks common to every call.
+int32_t check_dims(const mcs_dims* d) {
+  if (d == nullptr) return fail(MCS_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 1 || d->heads < 1)
+    return fail(MCS_ERR_INVALID_ARG, "batch (%d) and heads (%d) must be >= 1", d->batch, d->heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(MCS_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->group_size != 64 && d->group_size != 128)
+    return fail(MCS_ERR_UNSUPPORTED, "group_size %d not supported (64 or 128)", d->group_size);
+  if (d->n_pad < 1 || d->n_pad > (1 << 24))
+    return fail(MCS_ERR_UNSUPPORTED, "n_pad %d outside 1 .. 2^24", d->n_pad);
+  if (d->n_pad % d->group_size != 0)
+    return fail(MCS_ERR_INVALID_ARG, "n_pad %d is not a multiple of group_size %d", d->n_pad,
+                d->group_size);
+  if (d->n_valid < 1 || d->n_valid > d->n_pad)
+    return fail(MCS_ERR_INVALID_ARG, "n_valid %d outside 1 .. n_pad (%d)", d->n_valid, d->n_pad);
+  const double elems = (double)d->batch * d->heads * d->n_pad * d->head_dim;
+  if (elems >= 1099511627776.0)
+    return fail(MCS_ERR_UNSUPPORTED, "batch*heads*n_pad*head_dim too large");
+  const double items = (double)d->batch * d->heads * (d->n_pad / d->group_size);
+  if (items >= 2147483647.0) return fail(MCS_ERR_UNSUPPORTED, "too many groups for one launch");
+  return MCS_OK;
+}
+
+int32_t check_ptr(const void* p, const char* name, bool nullable = false) {
+  if (p == nullptr) {
+    if (nullable) return MCS_OK;
+    return fail(MCS_ERR_INVALID_ARG, "%s is NULL", name);
+  }
+  if (!aligned16(p)) return fail(MCS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MCS_OK;
+}
+
+int32_t check_topk(const mcs_dims* d, int32_t topk) {
+  if (topk < 1 || topk > d->n_valid)
+    return fail(MCS_ERR_INVALID_ARG, "topk %d outside 1 .. n_valid (%d)", topk, d->n_valid);
+  const double idx = (double)d->batch * d->heads * (d->n_pad / d->group_size) * topk;
+  if (idx >= 9.0e15) return fail(MCS_ERR_UNSUPPORTED, "kv_idx too large");
+  return MCS_OK;
+}
+
+int32_t check_scale(float s) {
+  if (!std::isfinite(s) || !(s > 0.f))
+    return fail(MCS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return MCS_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MCS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MCS_OK;
+}
+
+#define MCS_TRY(expr)            \
+  do {                           \
+    const int32_t _st = (expr);  \
+    if (_st != MCS_OK) return _st; \
+  } while (0)
+
+// ---- workspace layouts ----
+struct GroupWs {
+  size_t partial, mu, vec, proj, perm, total;
+};
+
+GroupWs group_ws(const mcs_dims* d) {
+  const size_t bh = (size_t)d->batch * d->heads;
+  const size_t G = (size_t)(d->n_pad / d->group_size);
+  GroupWs w;
+  size_t o = 0;
+  w.partial = o; o = align256(o + bh * G * d->head_dim * sizeof(double));
+  w.mu = o;      o = align256(o + bh * G * d->head_dim * sizeof(double));
+  w.vec = o;     o = align256(o + bh * G * d->head_dim * sizeof(double));
+  w.proj = o;    o = align256(o + bh * (size_t)d->n_pad * sizeof(double));
+  w.perm = o;    o = align256(o + bh * (size_t)d->n_pad * sizeof(int32_t));
+  w.total = o;
+  return w;
+}
+
+size_t scores_per_head(const mcs_dims* d) {
+  return align256((size_t)(d->n_pad / d->group_size) * d->n_valid * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mcs_abi_version(void) { return MCS_ABI_VERSION; }
+
+const char* mcs_status_string(int32_t s) {
+  switch (s) {
+    case MCS_OK: return "MCS_OK";
+    case MCS_ERR_INVALID_ARG: return "MCS_ERR_INVALID_ARG";
+    case MCS_ERR_UNSUPPORTED: return "MCS_ERR_UNSUPPORTED";
+    case MCS_ERR_WORKSPACE: return "MCS_ERR_WORKSPACE";
+    case MCS_ERR_HIP: return "MCS_ERR_HIP";
+    default: return "MCS_ERR_UNKNOWN";
+  }
+}
+
+const char* mcs_last_error(void) { return g_last_error.c_str(); }
+
+size_t mcs_group_workspace_bytes(const mcs_dims* dims) {
+  if (check_dims(dims) != MCS_OK) return 0;
+  return group_ws(dims).total;
+}
+
+int32_t mcs_group(const mcs_dims* dims, const uint16_t* q, int32_t power_iters,
+                  int32_t max_levels, int32_t* perm, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  MCS_TRY(check_dims(dims));
+  MCS_TRY(check_ptr(q, "q"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  if (power_iters < 0 || power_iters > 1000)
+    return fail(MCS_ERR_INVALID_ARG, "power_iters %d outside 0 .. 1000", power_iters);
+  const int G = dims->n_pad / dims->group_size;
+  const int L = levels_for(G);
+  if (max_levels < -1 || max_levels > L)
+    return fail(MCS_ERR_INVALID_ARG, "max_levels %d outside -1 .. %d", max_levels, L);
+  const GroupWs w = group_ws(dims);
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(MCS_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MCS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int levels = (max_levels < 0) ? L : max_levels;
+  int32_t* bufs[2] = {perm, (int32_t*)(ws + w.perm)};
+  // the last depth must land in `perm`
+  int cur = (levels % 2 == 0) ? 0 : 1;
+  mcs::PddpParams p{};
+  p.q = q;
+  p.partial = (double*)(ws + w.partial);
+  p.mu = (double*)(ws + w.mu);
+  p.vec = (double*)(ws + w.vec);
+  p.proj = (double*)(ws + w.proj);
+  p.bh = (int64_t)dims->batch * dims->heads;
+  p.n_pad = dims->n_pad;
+  p.groups = G;
+  p.perm_cur = bufs[cur];
+  p.perm_next = bufs[1 - cur];
+  MCS_TRY(hip_status(mcs::launch_pddp_identity(p, s), "pddp identity"));
+  const int d = dims->head_dim, c = dims->group_size;
+  for (int lv = 0; lv < levels; ++lv) {
+    p.level = lv;
+    p.perm_cur = bufs[cur];
+    p.perm_next = bufs[1 - cur];
+    MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 0, p, s), "pddp mean"));
+    MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 0, p, s), "pddp mean reduce"));
+    for (int it = 0; it < power_iters; ++it) {
+      MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 1, p, s), "pddp power step"));
+      MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 1, p, s), "pddp power reduce"));
+    }
+    MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 2, p, s), "pddp projection"));
+    MCS_TRY(hip_status(mcs::launch_pddp_split(c, p, s), "pddp split"));
+    cur = 1 - cur;
+  }
+  return ok();
+}
+
+size_t mcs_anchor_select_workspace_bytes(const mcs_dims* dims, int32_t topk) {
+  if (check_dims(dims) != MCS_OK || check_topk(dims, topk) != MCS_OK) return 0;
+  return scores_per_head(dims) * (size_t)dims->batch * dims->heads;
+}
+
+size_t mcs_anchor_select_min_workspace_bytes(const mcs_dims* dims, int32_t topk) {
+  if (check_dims(dims) != MCS_OK || check_topk(dims, topk) != MCS_OK) return 0;
+  return scores_per_head(dims);
+}
+
+int32_t mcs_dense_attn(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, float scale, uint16_t* o, float* lse, void* stream) {
+  MCS_TRY(check_dims(dims));
+  MCS_TRY(check_ptr(q, "q"));
+  MCS_TRY(check_ptr(k, "k"));
+  MCS_TRY(check_ptr(v, "v"));
+  MCS_TRY(check_ptr(o, "o"));
+  MCS_TRY(check_ptr(lse, "lse", true));
+  MCS_TRY(check_scale(scale));
+  mcs::AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = o; p.lse = lse;
+  p.bh = (int64_t)dims->batch * dims->heads;
+  p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
+  p.groups = dims->n_pad / dims->group_size;
+  p.scale = scale;
+  MCS_TRY(hip_status(mcs::launch_attention(mcs::ATTN_DENSE, dims->head_dim, dims->group_size, p,
+                                           (hipStream_t)stream),
+                     "dense attention"));
+  return ok();
+}
+
+int32_t mcs_anchor_select(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* v, const int32_t* perm, int32_t topk, float scale,
+                          uint16_t* o_full, float* lse, int32_t* kv_idx, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  MCS_TRY(check_dims(dims));
+  MCS_TRY(check_ptr(q, "q"));
+  MCS_TRY(check_ptr(k, "k"));
+  MCS_TRY(check_ptr(v, "v"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  MCS_TRY(check_ptr(o_full, "o_full"));
+  MCS_TRY(check_ptr(lse, "lse"));
+  MCS_TRY(check_ptr(kv_idx, "kv_idx"));
+  MCS_TRY(check_topk(dims, topk));
+  MCS_TRY(check_scale(scale));
+  const size_t per_head = scores_per_head(dims);
+  if (workspace == nullptr || workspace_bytes < per_head)
+    return fail(MCS_ERR_WORKSPACE, "workspace needs at least %zu bytes, got %zu", per_head,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MCS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t bh = (int64_t)dims->batch * dims->heads;
+  const int G = dims->n_pad / dims->group_size;
+
+  // pass 1: dense attention (O_full, lse)
+  mcs::AttnParams a{};
+  a.q = q; a.k = k; a.v = v; a.out = o_full; a.lse = lse;
+  a.bh = bh; a.n_valid = dims->n_valid; a.n_pad = dims->n_pad; a.groups = G; a.scale = scale;
+  MCS_TRY(hip_status(mcs::launch_attention(mcs::ATTN_DENSE, dims->head_dim, dims->group_size, a, s),
+                     "anchor pass 1"));
+
+  // pass 2 + top-k, as many heads at a time as the workspace holds
+  const int64_t chunk = std::min<int64_t>(bh, (int64_t)(workspace_bytes / per_head));
+  for (int64_t h0 = 0; h0 < bh; h0 += chunk) {
+    const int64_t hc = std::min<int64_t>(chunk, bh - h0);
+    mcs::ScoreParams sp{};
+    sp.q = q; sp.k = k; sp.perm = perm; sp.lse = lse; sp.scores = (float*)workspace;
+    sp.bh0 = h0; sp.bh_count = hc; sp.n_valid = dims->n_valid; sp.n_pad = dims->n_pad;
+    sp.groups = G; sp.scale = scale;
+    MCS_TRY(hip_status(mcs::launch_scores(dims->head_dim, dims->group_size, sp, s), "anchor pass 2"));
+    mcs::TopkParams tp{};
+    tp.scores = (const float*)workspace; tp.kv_idx = kv_idx; tp.bh0 = h0; tp.bh_count = hc;
+    tp.n_valid = dims->n_valid; tp.groups = G; tp.topk = topk;
+    MCS_TRY(hip_status(mcs::launch_topk(tp, s), "top-k"));
+  }
+  return ok();
+}
+
+static int32_t sparse_common(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                             int32_t topk, float scale) {
+  MCS_TRY(check_dims(dims));
+  MCS_TRY(check_ptr(q, "q"));
+  MCS_TRY(check_ptr(k, "k"));
+  MCS_TRY(check_ptr(v, "v"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  MCS_TRY(check_ptr(kv_idx, "kv_idx"));
+  MCS_TRY(check_topk(dims, topk));
+  MCS_TRY(check_scale(scale));
+  return MCS_OK;
+}
+
+int32_t mcs_residual(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, const int32_t* perm, const int32_t* kv_idx, int32_t topk,
+                     float scale, const uint16_t* o_full, uint16_t* r, void* stream) {
+  MCS_TRY(sparse_common(dims, q, k, v, perm, kv_idx, topk, scale));
+  MCS_TRY(check_ptr(o_full, "o_full"));
+  MCS_TRY(check_ptr(r, "r"));
+  mcs::AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.aux = o_full; p.out = r;
+  p.bh = (int64_t)dims->batch * dims->heads;
+  p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
+  p.groups = dims->n_pad / dims->group_size; p.topk = topk; p.scale = scale;
+  MCS_TRY(hip_status(mcs::launch_attention(mcs::ATTN_RESID, dims->head_dim, dims->group_size, p,
+                                           (hipStream_t)stream),
+                     "residual"));
+  return ok();
+}
+
+int32_t mcs_sparse_attn(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                        int32_t topk, float scale, const uint16_t* r, uint16_t* o, void* stream) {
+  MCS_TRY(sparse_common(dims, q, k, v, perm, kv_idx, topk, scale));
+  MCS_TRY(check_ptr(r, "r", true));
+  MCS_TRY(check_ptr(o, "o"));
+  if (o == q || o == k || o == v || (r != nullptr && o == r))
+    return fail(MCS_ERR_INVALID_ARG, "o must not alias q, k, v or r");
+  mcs::AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.aux = r; p.out = o;
+  p.bh = (int64_t)dims->batch * dims->heads;
+  p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
+  p.groups = dims->n_pad / dims->group_size; p.topk = topk; p.scale = scale;
+  MCS_TRY(hip_status(mcs::launch_attention(mcs::ATTN_SPARSE, dims->head_dim, dims->group_size, p,
+                                           (hipStream_t)stream),
+                     "sparse attention"));
+  return ok();
+}
+
+}  // extern "C"

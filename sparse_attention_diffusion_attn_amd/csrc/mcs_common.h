@@ -1,0 +1,104 @@
+// Device helpers shared by the gfx950 kernels: vector types, MFMA wrappers,
+// LDS swizzles, gathers straight into LDS, and the XCD-aware work mapping.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mcs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).  Lane l holds row/col
+// (l % 32) of A/B and the 8 k-slots 8*(l/32)+i; it receives D rows
+// 8*(j/4) + 4*(l/32) + (j%4), column l % 32, in accumulator j.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// K/V tiles of 64 rows live in LDS as D/32 "planes": plane T holds columns
+// 32T .. 32T+31 of all 64 rows, 64 bytes per row, 4 KiB per plane.  Inside a
+// plane the four 16-byte chunks of row r are permuted by XOR with (r >> 2) & 3.
+// With 64 four-byte banks this keeps conflict-free both the 16-byte reads of
+// 16 consecutive rows at one chunk (QK^T operand) and the transposing 8-byte
+// reads of 4 consecutive rows x 2 chunks (PV operand), and every LDS address a
+// lane uses is one of a few base registers plus a compile-time offset.
+__device__ __forceinline__ int plane_chunk(int row, int chunk4) {
+  return (chunk4 ^ (row >> 2)) & 3;
+}
+
+// Per-lane 16-byte global -> LDS copy; lane l's bytes land at lds_base + 16*l.
+__device__ __forceinline__ void gather16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane
+// j receives element (j % 4) of the 8-byte rows addressed by lanes j/4, j/4+4,
+// j/4+8 and j/4+12.  For every column plane T (4 KiB apart) this reads rows at
+// `pa` and at `pb` into out[2T] and out[2T+1], and waits for them before the
+// block ends (so no read is still in flight when its registers are used).
+template <int NPL>
+__device__ __forceinline__ void tr_read_planes(i32x2* out, const char* pa, const char* pb) {
+  const uint32_t a = (uint32_t)(uintptr_t)pa;
+  const uint32_t b = (uint32_t)(uintptr_t)pb;
+  if constexpr (NPL == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:8192\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:8192\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:12288\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:12288\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]),
+          "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7])
+        : "v"(a), "v"(b)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+        : "v"(a), "v"(b)
+        : "memory");
+  }
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs.  Map dispatch index i to a
+// work item so that each XCD receives one contiguous run of work items
+// (consecutive groups of the same head share that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int X = 8;
+  const int q = n / X, r = n % X;
+  const int x = i % X, j = i / X;
+  return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+}  // namespace mcs

@@ -1,0 +1,70 @@
+// Internal launch interface between the C-ABI layer (mcs_api.cpp) and the
+// gfx950 kernels (*.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mcs {
+
+enum AttnMode : int { ATTN_DENSE = 0, ATTN_SPARSE = 1, ATTN_RESID = 2 };
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* perm;    // sparse / resid: query rows of each group
+  const int32_t* kv_idx;  // sparse / resid: [BH, G, topk]
+  const uint16_t* aux;    // sparse: residual to add (nullable); resid: O_full
+  uint16_t* out;          // O (dense, sparse) or R (resid)
+  float* lse;             // dense: nullable
+  int64_t bh;             // batch * heads
+  int32_t n_valid, n_pad, groups, topk;
+  float scale;
+};
+
+struct ScoreParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const int32_t* perm;
+  const float* lse;
+  float* scores;          // [bh_count, G, n_valid]
+  int64_t bh0, bh_count;  // heads [bh0, bh0 + bh_count)
+  int32_t n_valid, n_pad, groups;
+  float scale;
+};
+
+struct TopkParams {
+  const float* scores;    // [bh_count, G, n_valid]
+  int32_t* kv_idx;        // [BH, G, topk], written for heads bh0 ..
+  int64_t bh0, bh_count;
+  int32_t n_valid, groups, topk;
+};
+
+struct PddpParams {
+  const uint16_t* q;
+  int32_t* perm_cur;      // current partition (read)
+  int32_t* perm_next;     // next partition (split writes)
+  double* partial;        // [BH, G, d]
+  double* mu;             // [BH, G, d]  indexed by node start group
+  double* vec;            // [BH, G, d]
+  double* proj;           // [BH, n_pad] by position
+  int64_t bh;
+  int32_t n_pad, groups, level;
+};
+
+hipError_t launch_attention(int mode, int head_dim, int group_size, const AttnParams& p,
+                            hipStream_t s);
+hipError_t launch_scores(int head_dim, int group_size, const ScoreParams& p, hipStream_t s);
+hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+
+hipError_t launch_pddp_identity(const PddpParams& p, hipStream_t s);
+// stage: 0 = node means, 1 = one power-iteration step, 2 = projections
+hipError_t launch_pddp_partial(int head_dim, int group_size, int stage, const PddpParams& p,
+                               hipStream_t s);
+// stage: 0 = finish means and set v0, 1 = finish a power-iteration step
+hipError_t launch_pddp_reduce(int head_dim, int group_size, int stage, const PddpParams& p,
+                              hipStream_t s);
+hipError_t launch_pddp_split(int group_size, const PddpParams& p, hipStream_t s);
+
+}  // namespace mcs

@@ -1,0 +1,121 @@
+"""The C-ABI library on the host: it loads, exports what include/mcs.h declares,
+and rejects bad arguments before touching the GPU (every call below fails
+validation, so nothing is enqueued and no GPU is needed)."""
+import ctypes
+
+import pytest
+
+import sparse_attention_diffusion_attn_amd as mcs
+
+P = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10008        # misaligned
+
+
+def d(batch=1, heads=2, n_valid=1000, n_pad=1024, head_dim=128, group_size=128):
+    return mcs.make_dims(batch, heads, n_valid, n_pad, head_dim, group_size)
+
+
+def err():
+    return mcs.lib().mcs_last_error().decode()
+
+
+def test_library_exports_every_header_symbol():
+    lib = mcs.lib()
+    names = mcs.header_functions()
+    assert set(names) >= {"mcs_group", "mcs_anchor_select", "mcs_residual", "mcs_sparse_attn",
+                          "mcs_dense_attn", "mcs_group_workspace_bytes",
+                          "mcs_anchor_select_workspace_bytes", "mcs_anchor_select_min_workspace_bytes",
+                          "mcs_status_string", "mcs_last_error", "mcs_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.mcs_abi_version() == 1
+    assert lib.mcs_status_string(3) == b"MCS_ERR_WORKSPACE"
+    assert lib.mcs_status_string(99) == b"MCS_ERR_UNKNOWN"
+
+
+def test_workspace_sizes():
+    lib = mcs.lib()
+    dm = d()
+    G, bh, D = 8, 2, 128
+    want = 0
+    for nbytes in (bh * G * D * 8,) * 3 + (bh * 1024 * 8, bh * 1024 * 4):
+        want = (want + nbytes + 255) // 256 * 256
+    assert lib.mcs_group_workspace_bytes(ctypes.byref(dm)) == want
+    per_head = (G * 1000 * 4 + 255) // 256 * 256
+    assert lib.mcs_anchor_select_min_workspace_bytes(ctypes.byref(dm), 250) == per_head
+    assert lib.mcs_anchor_select_workspace_bytes(ctypes.byref(dm), 250) == 2 * per_head
+    assert lib.mcs_anchor_select_workspace_bytes(ctypes.byref(dm), 0) == 0
+    assert lib.mcs_group_workspace_bytes(ctypes.byref(d(head_dim=96))) == 0
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(head_dim=96), mcs.MCS_ERR_UNSUPPORTED, "head_dim"),
+    (dict(group_size=32), mcs.MCS_ERR_UNSUPPORTED, "group_size"),
+    (dict(n_pad=1000, n_valid=900), mcs.MCS_ERR_INVALID_ARG, "multiple"),
+    (dict(n_valid=0), mcs.MCS_ERR_INVALID_ARG, "n_valid"),
+    (dict(n_valid=2000), mcs.MCS_ERR_INVALID_ARG, "n_valid"),
+    (dict(batch=0), mcs.MCS_ERR_INVALID_ARG, "batch"),
+    (dict(n_pad=1 << 25, n_valid=10), mcs.MCS_ERR_UNSUPPORTED, "n_pad"),
+])
+def test_bad_dims_rejected_by_every_call(kw, code, msg):
+    lib = mcs.lib()
+    dm = d(**kw)
+    b = ctypes.byref(dm)
+    calls = [
+        lambda: lib.mcs_group(b, P, 20, -1, P, P, 1 << 30, None),
+        lambda: lib.mcs_anchor_select(b, P, P, P, P, 5, 0.1, P, P, P, P, 1 << 30, None),
+        lambda: lib.mcs_residual(b, P, P, P, P, P, 5, 0.1, P, P, None),
+        lambda: lib.mcs_sparse_attn(b, P, P, P, P, P, 5, 0.1, None, P + 256, None),
+        lambda: lib.mcs_dense_attn(b, P, P, P, 0.1, P + 256, None, None),
+    ]
+    for c in calls:
+        assert c() == code
+        assert msg in err()
+
+
+def test_argument_checks():
+    lib = mcs.lib()
+    b = ctypes.byref(d())
+    # null and misaligned pointers
+    assert lib.mcs_sparse_attn(b, None, P, P, P, P, 5, 0.1, None, P + 256, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "q is NULL" in err()
+    assert lib.mcs_sparse_attn(b, P, MIS, P, P, P, 5, 0.1, None, P + 256, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "k is not 16-byte aligned" in err()
+    assert lib.mcs_dense_attn(b, P, P, P, 0.1, None, None, None) == mcs.MCS_ERR_INVALID_ARG
+    assert lib.mcs_residual(b, P, P, P, P, P, 5, 0.1, None, P, None) == mcs.MCS_ERR_INVALID_ARG
+    # topk range
+    for k in (0, 1001, -3):
+        assert lib.mcs_sparse_attn(b, P, P, P, P, P, k, 0.1, None, P + 256, None) == mcs.MCS_ERR_INVALID_ARG
+        assert "topk" in err()
+        assert lib.mcs_anchor_select(b, P, P, P, P, k, 0.1, P, P, P, P, 1 << 30, None) == mcs.MCS_ERR_INVALID_ARG
+    # scale
+    for sc in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.mcs_dense_attn(b, P, P, P, sc, P + 256, None, None) == mcs.MCS_ERR_INVALID_ARG
+        assert "scale" in err()
+    # aliasing output
+    assert lib.mcs_sparse_attn(b, P, P + 16, P + 32, P, P, 5, 0.1, None, P, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "alias" in err()
+    # grouping arguments
+    assert lib.mcs_group(b, P, -1, -1, P, P, 1 << 30, None) == mcs.MCS_ERR_INVALID_ARG
+    assert lib.mcs_group(b, P, 20, 4, P, P, 1 << 30, None) == mcs.MCS_ERR_INVALID_ARG  # L = 3
+    assert "max_levels" in err()
+
+
+def test_workspace_checks():
+    lib = mcs.lib()
+    dm = d()
+    b = ctypes.byref(dm)
+    need = lib.mcs_group_workspace_bytes(b)
+    assert lib.mcs_group(b, P, 20, -1, P, P, need - 1, None) == mcs.MCS_ERR_WORKSPACE
+    assert lib.mcs_group(b, P, 20, -1, P, None, need, None) == mcs.MCS_ERR_WORKSPACE
+    assert lib.mcs_group(b, P, 20, -1, P, P + 16, need, None) == mcs.MCS_ERR_WORKSPACE
+    assert "256-byte" in err()
+    mn = lib.mcs_anchor_select_min_workspace_bytes(b, 5)
+    assert lib.mcs_anchor_select(b, P, P, P, P, 5, 0.1, P, P, P, P, mn - 1, None) == mcs.MCS_ERR_WORKSPACE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mcs.dense_attn(q, q, q, 128, 64)
