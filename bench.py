@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the MC-Sparse attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic layer: the anchor
+step (mcs_group -> mcs_anchor_select -> mcs_residual) followed by the layer's
+reuse steps (mcs_sparse_attn on drifted Q/K/V, cached metadata).  Default
+workload: the 480p video-DiT layer (B1 H24 N32760 -> 32768, d128, C128, 25%
+density, k = 8190, 1 anchor + 4 reuse steps).
+
+Headline metric: effective TFLOP/s of the reuse-step sparse attention
+(4*B*H*N_pad*k*d executed flops / kernel time, HIP events on the launch
+stream), and the achieved fraction of the ideal 1/s speed-up over this build's
+own dense kernel (mcs_dense_attn) at the same shape: (k/N) * t_dense / t_sparse.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 480p]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="480p")
+    ap.add_argument("--ratio-reps", type=int, default=10, help="reps of the dense-vs-sparse timing")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["sparse", "dense", "anchor"], default=None,
+                    help="profile helper: run only this call in a loop (no JSON line)")
+    return ap.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_attention_diffusion_attn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_src_hash):
+    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE and
+    WRITE_SIZE), stored with the hash of the kernel source it was taken on."""
+    path = os.path.join(ROOT, "profiles", "sparse_attn_480p_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_hash") != kernel_src_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, q, k, v, perm, kv, budget_s):
+    """The fp64 oracle's sparse attention on the first query groups of the
+    layer (as many as fit in `budget_s`), one thread; returns its effective
+    TFLOP/s in the metric's unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import mcs_oracle as orc
+
+    flops_per_group = 4.0 * cfg.group_size * cfg.topk * cfg.head_dim
+    perm_h, kv_h = perm.cpu().numpy(), kv.cpu().numpy()
+    done, heads, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        for h in range(cfg.heads):
+            qh = q[0, h].float().numpy().astype(np.float64)
+            kh = k[0, h].float().numpy().astype(np.float64)
+            vh = v[0, h].float().numpy().astype(np.float64)
+            heads += 1
+            for g in range(cfg.groups):
+                orc.sparse_attention(qh, kh, vh, perm_h[0, h], kv_h[0, h][[g]], cfg.n_valid,
+                                     cfg.group_size, cfg.scale, groups=[g])
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": flops_per_group * done / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 oracle sparse attention of {done} query groups (C={cfg.group_size}, "
+                      f"k={cfg.topk}, d={cfg.head_dim}) from the first {heads} head(s) of the same layer "
+                      f"(reuse step 1, the GPU's metadata), one thread, "
+                      f"{dt:.1f} s; host {platform.processor() or platform.machine()}, "
+                      f"{os.cpu_count()} logical CPUs visible"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "heads shard across GPUs with no exchange, which is not exercised here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_diffusion_attn_amd as mcs
+    import synthdata as sd
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mcs.lib()
+    dev = torch.device("cuda:0")
+    cfg = sd.CONFIGS[args.config]
+    B, H, nv, n_pad, d, C, k = cfg.batch, cfg.heads, cfg.n_valid, cfg.n_pad, cfg.head_dim, cfg.group_size, cfg.topk
+    sc = cfg.scale
+    t_gen = time.perf_counter()
+    steps_cpu = sd.generate(cfg)
+    print(f"# generated {len(steps_cpu)} steps of {cfg.name} in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    steps = [tuple(t.to(dev) for t in s) for s in steps_cpu]
+    q0, k0, v0 = steps[0]
+    dims = mcs.make_dims(B, H, nv, n_pad, d, C)
+    G = cfg.groups
+    perm = torch.empty((B, H, n_pad), dtype=torch.int32, device=dev)
+    o_full = torch.empty_like(q0)
+    lse = torch.empty((B, H, n_pad), dtype=torch.float32, device=dev)
+    kv = torch.empty((B, H, G, k), dtype=torch.int32, device=dev)
+    r = torch.empty_like(q0)
+    outs = [torch.empty_like(q0) for _ in steps[1:]]
+    ws_g = torch.empty(mcs.group_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(mcs.anchor_select_workspace_bytes(dims, k), dtype=torch.uint8, device=dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    stage_names = ["group", "anchor_select", "residual", "sparse_attn"]
+
+    def one_step(record):
+        marks = []
+        e = ev(); e.record(); marks.append(e)
+        mcs.group(q0, nv, C, cfg.power_iters, perm=perm, workspace=ws_g)
+        e = ev(); e.record(); marks.append(e)
+        mcs.anchor_select(q0, k0, v0, perm, nv, C, k, sc, o_full=o_full, lse=lse, kv_idx=kv, workspace=ws_a)
+        e = ev(); e.record(); marks.append(e)
+        mcs.residual(q0, k0, v0, perm, kv, o_full, nv, C, sc, r=r)
+        e = ev(); e.record(); marks.append(e)
+        for (qt, kt, vt), o in zip(steps[1:], outs):
+            mcs.sparse_attn(qt, kt, vt, perm, kv, r, nv, C, sc, o=o)
+            e = ev(); e.record(); marks.append(e)
+        record.append(marks)
+
+    if args.only:
+        # profiling helper: warm up the metadata, then loop one call
+        one_step([])
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            if args.only == "sparse":
+                mcs.sparse_attn(steps[1][0], steps[1][1], steps[1][2], perm, kv, r, nv, C, sc, o=outs[0])
+            elif args.only == "dense":
+                mcs.dense_attn(q0, k0, v0, nv, C, sc, o=o_full, lse=lse)
+            else:
+                mcs.anchor_select(q0, k0, v0, perm, nv, C, k, sc, o_full=o_full, lse=lse, kv_idx=kv, workspace=ws_a)
+        torch.cuda.synchronize()
+        print(f"# ran {args.steps} x {args.only}", file=sys.stderr)
+        return
+
+    for _ in range(args.warmup):
+        one_step([])
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    stage_ms = {n: [] for n in stage_names}
+    for marks in recs:
+        stage_ms["group"].append(marks[0].elapsed_time(marks[1]))
+        stage_ms["anchor_select"].append(marks[1].elapsed_time(marks[2]))
+        stage_ms["residual"].append(marks[2].elapsed_time(marks[3]))
+        for i in range(3, len(marks) - 1):
+            stage_ms["sparse_attn"].append(marks[i].elapsed_time(marks[i + 1]))
+    t_sparse_ms = statistics.mean(stage_ms["sparse_attn"])
+    sparse_flops = 4.0 * B * H * n_pad * k * d
+    eff_tflops = sparse_flops / (t_sparse_ms * 1e-3) / 1e12
+    print(f"# step {ms_per_step:.2f} ms; stages (ms): " +
+          ", ".join(f"{n} {statistics.mean(v):.3f}" for n, v in stage_ms.items()), file=sys.stderr, flush=True)
+
+    # sanity: the reuse outputs are finite and padded rows are zero
+    for o in outs:
+        assert torch.isfinite(o.float()).all().item()
+        assert (o[:, :, nv:] == 0).all().item()
+
+    # dense vs sparse at the same shape, identical protocol: a 512 MiB write
+    # evicts L2 / MALL before each timed call.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    q1, k1, v1 = steps[1]
+    o_d = torch.empty_like(q0)
+    t_d, t_s = [], []
+    for _ in range(args.ratio_reps):
+        for which in ("dense", "sparse"):
+            flush.fill_(1)
+            a, b = ev(), ev()
+            a.record()
+            if which == "dense":
+                mcs.dense_attn(q1, k1, v1, nv, C, sc, o=o_d, want_lse=False)
+            else:
+                mcs.sparse_attn(q1, k1, v1, perm, kv, r, nv, C, sc, o=outs[0])
+            b.record()
+            torch.cuda.synchronize()
+            (t_d if which == "dense" else t_s).append(a.elapsed_time(b))
+    td, ts = statistics.median(t_d), statistics.median(t_s)
+    density = k / nv
+    ideal_frac = density * td / ts
+    dense_flops = 4.0 * B * H * n_pad * nv * d
+    dense_tflops = dense_flops / (td * 1e-3) / 1e12
+
+    kernel_hash = source_hash("attn.hip", "mcs_common.h")
+    traffic = load_traffic(kernel_hash)
+    roofline = {"bound": "mfma", "achieved": round(eff_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(eff_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "attn_kernel<128,128,SPARSE> (mcs_sparse_attn)",
+                "flops_per_launch": sparse_flops, "avg_launch_ms": round(t_sparse_ms, 4),
+                "kernel_src_hash": kernel_hash}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, steps_cpu[1][0], steps_cpu[1][1], steps_cpu[1][2], perm, kv, args.cpu_seconds)
+
+    anchor_ms = (statistics.mean(stage_ms["group"]) + statistics.mean(stage_ms["anchor_select"]) +
+                 statistics.mean(stage_ms["residual"]))
+    line = {
+        "metric": "sparse-attn effective TFLOP/s + % of ideal 1/s speedup vs dense, at 15/25% density",
+        "value": round(eff_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded clustered Q/K, Gaussian V; no model weights)",
+        "config": {
+            "workload": f"{cfg.name} video-DiT attention layer: B{B} H{H} N{nv}->{n_pad} d{d} C{C} "
+                        f"density {cfg.density_pct}% (k={k}), 1 anchor + {cfg.n_reuse} reuse steps per step",
+            "batch": B, "heads": H, "n_valid": nv, "n_pad": n_pad, "head_dim": d, "group_size": C,
+            "topk": k, "density_pct": cfg.density_pct, "reuse_steps": cfg.n_reuse,
+            "power_iters": cfg.power_iters, "parallelism": "single GPU"},
+        "ideal_1_over_s_frac": round(ideal_frac, 4),
+        "dense_ms": round(td, 4),
+        "sparse_ms": round(ts, 4),
+        "dense_tflops": round(dense_tflops, 2),
+        "dense_mfma_frac": round(dense_tflops / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {n: round(statistics.mean(v), 4) for n, v in stage_ms.items()},
+        # extra anchor work over a dense step, spread over the anchor's steps,
+        # in units of the dense step (density-equivalent overhead)
+        "anchor_overhead_ds": round((anchor_ms - td) / (cfg.n_reuse + 1) / td, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
