@@ -20,6 +20,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no accvgpr moves around the softmax)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
 ]
 

@@ -24,6 +24,9 @@
 
 namespace mcs {
 
+// Headroom of the lazily updated running max, in log2 units.
+constexpr float kLazyLog2 = 8.0f;
+
 template <int D, int C, int MODE>
 __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   constexpr int NW = C / 32;            // wavefronts, 32 query rows each
@@ -158,17 +161,28 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
     }
 
     // online softmax (this lane owns query ql; its partner lane ql+32 holds
-    // the other half of the tile's keys)
+    // the other half of the tile's keys).  The running max is only raised when
+    // the tile's max exceeds it by more than kLazyLog2 (in log2 units), so the
+    // rescale of O and l is skipped on almost every tile; probabilities stay
+    // below 2^kLazyLog2 and the final O / l is unchanged.
     float mx = s0[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s0[j]);
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s1[j]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx);
-    const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c2);
-    mrun = mnew;
-    const float mc = mnew * c2;
+    const bool raise = (mx - mrun) * c2 > kLazyLog2;
+    if (__any(raise)) {
+      const float mnew = raise ? mx : mrun;
+      const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c2);
+      mrun = mnew;
+      lrun *= alpha;
+#pragma unroll
+      for (int T = 0; T < NPL; ++T)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[T][j] *= alpha;
+    }
+    const float mc = mrun * c2;
     float ls = 0.f;
     bf16x8 pb[4];
 #pragma unroll
@@ -179,11 +193,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
       pb[j >> 3][j & 7] = (__bf16)e0;
       pb[2 + (j >> 3)][j & 7] = (__bf16)e1;
     }
-    lrun = lrun * alpha + ls;
-#pragma unroll
-    for (int T = 0; T < NPL; ++T)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) o[T][j] *= alpha;
+    lrun += ls;
 
     // O^T += V^T . P^T.  The transposing reads are issued from inline asm
     // (with their wait inside the same block) so that the compiler does not
