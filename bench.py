@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--ratio-reps", type=int, default=10, help="reps of the dense-vs-sparse timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["sparse", "dense", "anchor"], default=None,
+    ap.add_argument("--only", choices=["sparse", "dense", "anchor", "group", "copy"], default=None,
                     help="profile helper: run only this call in a loop (no JSON line)")
     return ap.parse_args()
 
@@ -152,6 +152,16 @@ def main():
             e = ev(); e.record(); marks.append(e)
         record.append(marks)
 
+    if args.only == "copy":
+        # profiling helper: a plain 1 GiB device copy, to calibrate the HBM
+        # byte counters against a kernel of known traffic
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# ran {args.steps} x 1 GiB copy", file=sys.stderr)
+        return
     if args.only:
         # profiling helper: warm up the metadata, then loop one call
         one_step([])
@@ -159,6 +169,8 @@ def main():
         for _ in range(args.steps):
             if args.only == "sparse":
                 mcs.sparse_attn(steps[1][0], steps[1][1], steps[1][2], perm, kv, r, nv, C, sc, o=outs[0])
+            elif args.only == "group":
+                mcs.group(q0, nv, C, cfg.power_iters, perm=perm, workspace=ws_g)
             elif args.only == "dense":
                 mcs.dense_attn(q0, k0, v0, nv, C, sc, o=o_full, lse=lse)
             else:
