@@ -42,7 +42,7 @@ def softmax_scale(d: int) -> float:
 # ---------------------------------------------------------------------------
 # O2  dense attention (anchor pass 1)
 # ---------------------------------------------------------------------------
-def dense_attention(q, k, v, n_valid, scale, block=256):
+def dense_attention(q, k, v, n_valid, scale, block=256, rows=None):
     """Dense softmax attention and its log-sum-exp.
 
     [onedev] "what is different": at the anchor step dense attention is run and
@@ -52,22 +52,25 @@ def dense_attention(q, k, v, n_valid, scale, block=256):
     s_ij = scale * q_i . k_j over keys j < n_valid (padded keys never take
     part); LSE_i = log sum_j exp(s_ij) (natural log); O_i = sum_j
     exp(s_ij - LSE_i) v_j.  Rows i >= n_valid (padding) get O = 0 and LSE = 0.
-    Row blocks only bound memory; each row is computed on its own.
+    Row blocks only bound memory; each row is computed on its own.  With
+    `rows` (token indices), only those rows are computed and returned, in the
+    order given.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)[:n_valid]
     v = np.asarray(v, np.float64)[:n_valid]
-    n_pad, d = q.shape
-    o = np.zeros((n_pad, v.shape[1]))
-    lse = np.zeros(n_pad)
-    for r0 in range(0, n_valid, block):
-        r1 = min(n_valid, r0 + block)
-        s = scale * (q[r0:r1] @ k.T)
+    idx = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    o = np.zeros((len(idx), v.shape[1]))
+    lse = np.zeros(len(idx))
+    live = np.nonzero(idx < n_valid)[0]
+    for b0 in range(0, len(live), block):
+        sel = live[b0:b0 + block]
+        s = scale * (q[idx[sel]] @ k.T)
         m = s.max(axis=1, keepdims=True)
         l = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
         p = np.exp(s - l[:, None])
-        o[r0:r1] = p @ v
-        lse[r0:r1] = l
+        o[sel] = p @ v
+        lse[sel] = l
     return o, lse
 
 

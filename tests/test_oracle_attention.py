@@ -49,6 +49,15 @@ def test_dense_matches_torch_sdpa(n, n_valid, d):
     np.testing.assert_allclose(lse[:n_valid], ref_lse, atol=1e-12)
 
 
+def test_dense_row_subset_matches_full():
+    q, k, v = rand_head(160, 16, 21, 150)
+    o, lse = orc.dense_attention(q, k, v, 150, 0.25)
+    rows = np.array([155, 3, 149, 77, 0])
+    o2, l2 = orc.dense_attention(q, k, v, 150, 0.25, rows=rows)
+    np.testing.assert_array_equal(o2, o[rows])
+    np.testing.assert_array_equal(l2, lse[rows])
+
+
 def test_dense_closed_form_two_keys():
     g = GOLD["two_key_attention"]
     q, k, v = (np.array(g[x], np.float64) for x in ("q", "k", "v"))
