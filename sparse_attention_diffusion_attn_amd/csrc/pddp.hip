@@ -82,9 +82,12 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
     // column sums; thread (d, part) sums rows part, part + NT/D, ...
     constexpr int PARTS = NT / D;
     const int d = tid % D, part = tid / D;
-    double acc = 0.0;
-    for (int r = part; r < C; r += PARTS) acc += (double)bf16_to_f32(xs[r * D + d]);
-    half[tid] = acc;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int r = part; r < C; r += 4 * PARTS) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += (double)bf16_to_f32(xs[(r + e * PARTS) * D + d]);
+    }
+    half[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
     if (tid < D) {
       double tot = half[tid];
@@ -111,14 +114,28 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
     __syncthreads();
   }
 
-  // t_r = (x_r - mu) . v : TPR threads per row, contiguous dimension slices
+  // t_r = (x_r - mu) . v : TPR threads per row, each on a slice of SL
+  // dimensions read 4 at a time into 4 accumulators, visited from a
+  // row-dependent start so that the lanes of a wavefront (different rows,
+  // same row stride) spread over the LDS banks
   {
     const int r = tid / TPR, part = tid % TPR;
     constexpr int SL = D / TPR;
-    double acc = 0.0;
-    for (int d = part * SL; d < (part + 1) * SL; ++d)
-      acc += ((double)bf16_to_f32(xs[r * D + d]) - mus[d]) * vs[d];
-    half[tid] = acc;
+    constexpr int NG = SL / 4;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int i = 0; i < NG; ++i) {
+      const int d = part * SL + 4 * ((i + r) & (NG - 1));
+      const uint2 xv = *(const uint2*)(xs + r * D + d);
+      const double x0 = (double)__uint_as_float(xv.x << 16);
+      const double x1 = (double)__uint_as_float(xv.x & 0xffff0000u);
+      const double x2 = (double)__uint_as_float(xv.y << 16);
+      const double x3 = (double)__uint_as_float(xv.y & 0xffff0000u);
+      acc[0] = __builtin_fma(x0 - mus[d], vs[d], acc[0]);
+      acc[1] = __builtin_fma(x1 - mus[d + 1], vs[d + 1], acc[1]);
+      acc[2] = __builtin_fma(x2 - mus[d + 2], vs[d + 2], acc[2]);
+      acc[3] = __builtin_fma(x3 - mus[d + 3], vs[d + 3], acc[3]);
+    }
+    half[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
     if (part == 0) {
       double t = half[tid];
@@ -135,10 +152,16 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   {
     constexpr int PARTS = NT / D;
     const int d = tid % D, part = tid / D;
-    double acc = 0.0;
-    for (int r = part; r < C; r += PARTS)
-      acc += ts[r] * ((double)bf16_to_f32(xs[r * D + d]) - mus[d]);
-    half[tid] = acc;
+    const double mud = mus[d];
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int r = part; r < C; r += 4 * PARTS) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = r + e * PARTS;
+        acc[e] = __builtin_fma(ts[rr], (double)bf16_to_f32(xs[rr * D + d]) - mud, acc[e]);
+      }
+    }
+    half[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
     if (tid < D) {
       double tot = half[tid];
