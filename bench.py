@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--ratio-reps", type=int, default=10, help="reps of the dense-vs-sparse timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--reuse", type=int, default=None,
+                    help="reuse steps per bench step (default: the layer config's own count)")
     ap.add_argument("--only", choices=["sparse", "dense", "anchor", "group", "copy"], default=None,
                     help="profile helper: run only this call in a loop (no JSON line)")
     return ap.parse_args()
@@ -116,6 +118,9 @@ def main():
     mcs.lib()
     dev = torch.device("cuda:0")
     cfg = sd.CONFIGS[args.config]
+    if args.reuse is not None:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, n_reuse=args.reuse)
     B, H, nv, n_pad, d, C, k = cfg.batch, cfg.heads, cfg.n_valid, cfg.n_pad, cfg.head_dim, cfg.group_size, cfg.topk
     sc = cfg.scale
     t_gen = time.perf_counter()
@@ -207,15 +212,16 @@ def main():
         assert torch.isfinite(o.float()).all().item()
         assert (o[:, :, nv:] == 0).all().item()
 
-    # dense vs sparse at the same shape, identical protocol: a 512 MiB write
-    # evicts L2 / MALL before each timed call.
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # dense vs sparse at the same shape, identical protocol: a read of a
+    # 512 MiB buffer evicts L2 / MALL before each timed call (a read, so no
+    # dirty lines are left to be written back during the timed kernel).
+    flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
     q1, k1, v1 = steps[1]
     o_d = torch.empty_like(q0)
     t_d, t_s = [], []
     for _ in range(args.ratio_reps):
         for which in ("dense", "sparse"):
-            flush.fill_(1)
+            flush_sum = flush.sum()
             a, b = ev(), ev()
             a.record()
             if which == "dense":
