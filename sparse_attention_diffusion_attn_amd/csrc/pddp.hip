@@ -34,6 +34,30 @@ __device__ __forceinline__ void node_of(int G, int level, int g, int& s, int& m)
   }
 }
 
+// Node numbered `slot` (0 .. 2^level - 1, the path bits from the root, left =
+// 0) at tree depth `level`.  A one-group leaf is carried down as its own left
+// child, so every node of the depth has exactly one slot; other slots are
+// empty (returns false).
+__device__ __forceinline__ bool node_of_slot(int G, int level, int slot, int& s, int& m) {
+  s = 0;
+  m = G;
+  for (int b = level - 1; b >= 0; --b) {
+    const int bit = (slot >> b) & 1;
+    if (m < 2) {
+      if (bit) return false;
+      continue;
+    }
+    const int hh = m >> 1;
+    if (bit == 0) {
+      m = hh;
+    } else {
+      s += hh;
+      m -= hh;
+    }
+  }
+  return true;
+}
+
 __global__ void pddp_identity_kernel(int32_t* perm, int n_pad, int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < total) perm[i] = (int32_t)(i % n_pad);
@@ -45,11 +69,13 @@ __global__ void pddp_identity_kernel(int32_t* perm, int n_pad, int64_t total) {
 template <int D, int C, int STAGE>
 __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   constexpr int NT = 256;
-  constexpr int TPR = NT / C;  // threads per row for dot products
-  __shared__ uint16_t xs[C * D];
+  // thread (dg, rg) works on dimensions 8dg .. 8dg+7 of rows rg, rg+RG, ...
+  constexpr int DG = D / 8, RG = NT / DG, RPT = C / RG;
+  constexpr int TP = DG + 1;  // padded row of per-row partial dot products
+  __shared__ __attribute__((aligned(16))) uint16_t xs[C * D];
   __shared__ double mus[D], vs[D];
   __shared__ double ts[C];
-  __shared__ double half[NT];
+  __shared__ double part[(C * TP > RG * D) ? C * TP : RG * D];
   __shared__ int flip;
 
   const int G = p.groups;
@@ -60,13 +86,28 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   node_of(G, p.level, g, s, m);
   if (m < 2) return;
   const int tid = threadIdx.x;
+  const int dg = tid % DG, rg = tid / DG;
   const int32_t* pc = p.perm_cur + (size_t)bh * p.n_pad + (size_t)g * C;
   const uint16_t* Qb = p.q + (size_t)bh * p.n_pad * D;
 
-  // stage the block's C rows (bf16) in LDS, 16 bytes per thread per step
-  for (int e = tid; e < C * D / 8; e += NT) {
-    const int r = e / (D / 8), c8 = e % (D / 8);
-    *(uint4*)(xs + r * D + c8 * 8) = *(const uint4*)(Qb + (size_t)pc[r] * D + c8 * 8);
+  // stage the block's C rows (bf16) in LDS: all row indices first, then all
+  // 16-byte loads, then the LDS stores (one round trip for each)
+  {
+    constexpr int NL = C * D / 8 / NT;
+    int rows[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) rows[k] = pc[(tid + k * NT) / (D / 8)];
+    uint4 vals[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int c8 = (tid + k * NT) % (D / 8);
+      vals[k] = *(const uint4*)(Qb + (size_t)rows[k] * D + c8 * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int e = tid + k * NT;
+      *(uint4*)(xs + (e / (D / 8)) * D + (e % (D / 8)) * 8) = vals[k];
+    }
   }
   if (STAGE > 0) {
     const double* mu = p.mu + ((size_t)bh * G + s) * D;
@@ -78,22 +119,40 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   }
   __syncthreads();
 
-  if (STAGE == 0) {
-    // column sums; thread (d, part) sums rows part, part + NT/D, ...
-    constexpr int PARTS = NT / D;
-    const int d = tid % D, part = tid / D;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int r = part; r < C; r += 4 * PARTS) {
+  // eight bf16 of row r, dimensions 8dg .. 8dg+7, as doubles
+  auto row8 = [&](int r, double (&x)[8]) {
+    const uint4 xv = *(const uint4*)(xs + r * D + 8 * dg);
+    const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += (double)bf16_to_f32(xs[(r + e * PARTS) * D + d]);
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = (double)__uint_as_float(w4[e] << 16);
+      x[2 * e + 1] = (double)__uint_as_float(w4[e] & 0xffff0000u);
     }
-    half[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    __syncthreads();
+  };
+  // column partials part[rg][d] -> fixed-order sum over rg, for d = tid < D
+  auto column_total = [&]() {
+    double tot = 0.0;
     if (tid < D) {
-      double tot = half[tid];
-      for (int q = 1; q < PARTS; ++q) tot += half[q * D + tid];
-      p.partial[((size_t)bh * G + g) * D + tid] = tot;
+      tot = part[tid];
+      for (int q = 1; q < RG; ++q) tot += part[q * D + tid];
     }
+    return tot;
+  };
+
+  if (STAGE == 0) {
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      double x[8];
+      row8(rg + k * RG, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rg * D + 8 * dg + e] = acc[e];
+    __syncthreads();
+    const double tot = column_total();
+    if (tid < D) p.partial[((size_t)bh * G + g) * D + tid] = tot;
     return;
   }
 
@@ -114,60 +173,55 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
     __syncthreads();
   }
 
-  // t_r = (x_r - mu) . v : TPR threads per row, each on a slice of SL
-  // dimensions read 4 at a time into 4 accumulators, visited from a
-  // row-dependent start so that the lanes of a wavefront (different rows,
-  // same row stride) spread over the LDS banks
-  {
-    const int r = tid / TPR, part = tid % TPR;
-    constexpr int SL = D / TPR;
-    constexpr int NG = SL / 4;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int i = 0; i < NG; ++i) {
-      const int d = part * SL + 4 * ((i + r) & (NG - 1));
-      const uint2 xv = *(const uint2*)(xs + r * D + d);
-      const double x0 = (double)__uint_as_float(xv.x << 16);
-      const double x1 = (double)__uint_as_float(xv.x & 0xffff0000u);
-      const double x2 = (double)__uint_as_float(xv.y << 16);
-      const double x3 = (double)__uint_as_float(xv.y & 0xffff0000u);
-      acc[0] = __builtin_fma(x0 - mus[d], vs[d], acc[0]);
-      acc[1] = __builtin_fma(x1 - mus[d + 1], vs[d + 1], acc[1]);
-      acc[2] = __builtin_fma(x2 - mus[d + 2], vs[d + 2], acc[2]);
-      acc[3] = __builtin_fma(x3 - mus[d + 3], vs[d + 3], acc[3]);
-    }
-    half[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    __syncthreads();
-    if (part == 0) {
-      double t = half[tid];
-      for (int q = 1; q < TPR; ++q) t += half[tid + q];
-      ts[r] = t;
-    }
-    __syncthreads();
+  double mu8[8], v8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mu8[e] = mus[8 * dg + e];
+    v8[e] = vs[8 * dg + e];
   }
+  // t_r = (x_r - mu) . v: partial dot products over each thread's 8
+  // dimensions, then a fixed-order sum over the DG partials of each row
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int r = rg + k * RG;
+    double x[8];
+    row8(r, x);
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      a0 = __builtin_fma(x[e] - mu8[e], v8[e], a0);
+      a1 = __builtin_fma(x[e + 1] - mu8[e + 1], v8[e + 1], a1);
+    }
+    part[r * TP + dg] = a0 + a1;
+  }
+  __syncthreads();
+  if (tid < C) {
+    double t = part[tid * TP];
+    for (int q = 1; q < DG; ++q) t += part[tid * TP + q];
+    ts[tid] = t;
+  }
+  __syncthreads();
   if (STAGE == 2) {
     if (tid < C) p.proj[(size_t)bh * p.n_pad + (size_t)g * C + tid] = ts[tid];
     return;
   }
   // w_d = sum_r t_r (x_rd - mu_d)
   {
-    constexpr int PARTS = NT / D;
-    const int d = tid % D, part = tid / D;
-    const double mud = mus[d];
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int r = part; r < C; r += 4 * PARTS) {
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = r + e * PARTS;
-        acc[e] = __builtin_fma(ts[rr], (double)bf16_to_f32(xs[rr * D + d]) - mud, acc[e]);
-      }
+    for (int k = 0; k < RPT; ++k) {
+      const int r = rg + k * RG;
+      const double t = ts[r];
+      double x[8];
+      row8(r, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(t, x[e] - mu8[e], acc[e]);
     }
-    half[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rg * D + 8 * dg + e] = acc[e];
     __syncthreads();
-    if (tid < D) {
-      double tot = half[tid];
-      for (int q = 1; q < PARTS; ++q) tot += half[q * D + tid];
-      p.partial[((size_t)bh * G + g) * D + tid] = tot;
-    }
+    const double tot = column_total();
+    if (tid < D) p.partial[((size_t)bh * G + g) * D + tid] = tot;
   }
 }
 
@@ -180,11 +234,10 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
   __shared__ double part_sum[NT];
   __shared__ double sq[NT];
   const int G = p.groups;
-  const int64_t bh = blockIdx.x / G;
-  const int g = blockIdx.x - (int)(bh * G);
+  const int slots = 1 << p.level;
+  const int64_t bh = blockIdx.x / slots;
   int s, m;
-  node_of(G, p.level, g, s, m);
-  if (g != s || m < 2) return;
+  if (!node_of_slot(G, p.level, blockIdx.x - (int)(bh * slots), s, m) || m < 2) return;
   const int tid = threadIdx.x;
   const int d = tid % D, part = tid / D;
   // groups s + part, s + part + PARTS, ... in order
@@ -255,11 +308,10 @@ __global__ __launch_bounds__(512) void pddp_split_kernel(PddpParams p) {
   __shared__ int scan_sh[NT / 64 + 1];
   __shared__ int found[2];
   const int G = p.groups;
-  const int64_t bh = blockIdx.x / G;
-  const int g = blockIdx.x - (int)(bh * G);
+  const int slots = 1 << p.level;
+  const int64_t bh = blockIdx.x / slots;
   int s, m;
-  node_of(G, p.level, g, s, m);
-  if (g != s) return;
+  if (!node_of_slot(G, p.level, blockIdx.x - (int)(bh * slots), s, m)) return;
   const int tid = threadIdx.x;
   const int32_t* pc = p.perm_cur + (size_t)bh * p.n_pad + (size_t)s * C;
   int32_t* pn = p.perm_next + (size_t)bh * p.n_pad + (size_t)s * C;
@@ -390,7 +442,7 @@ hipError_t launch_pddp_partial(int d, int c, int stage, const PddpParams& p, hip
 
 template <int D, int C>
 static hipError_t reduce_t(int stage, const PddpParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.bh * p.groups));
+  const dim3 grid((unsigned)(p.bh << p.level));
   if (stage == 0) hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 0>), grid, dim3(256), 0, s, p);
   else hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 1>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
@@ -405,7 +457,7 @@ hipError_t launch_pddp_reduce(int d, int c, int stage, const PddpParams& p, hipS
 }
 
 hipError_t launch_pddp_split(int c, const PddpParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.bh * p.groups));
+  const dim3 grid((unsigned)(p.bh << p.level));
   if (c == 128) hipLaunchKernelGGL((pddp_split_kernel<128>), grid, dim3(512), 0, s, p);
   else if (c == 64) hipLaunchKernelGGL((pddp_split_kernel<64>), grid, dim3(512), 0, s, p);
   else return hipErrorInvalidValue;
