@@ -32,7 +32,7 @@
  * padded keys never take part in a softmax and are never selected; padded
  * query rows take part in grouping as all-zero rows and get O = R = 0, lse = 0.
  * Supported: head_dim in {64, 128}; group_size C in {64, 128}; n_pad a
- * multiple of C; 1 <= n_valid <= n_pad <= 2^24; 1 <= topk <= n_valid;
+ * multiple of C; 1 <= n_valid <= n_pad < 2^24; 1 <= topk <= n_valid;
  * batch*heads*n_pad*head_dim < 2^40.  Every pointer must be 16-byte aligned.
  *
  * Ownership: the caller allocates every buffer, workspaces included.  The

@@ -8,7 +8,7 @@
 //
 // One workgroup per (head, query group): C/32 wavefronts, each owning 32 query
 // rows.  Key/value tiles of 64 rows are gathered by index with 16-byte
-// global->LDS copies into a double-buffered LDS tile (column planes, chunks
+// buffer->LDS copies into a double-buffered LDS tile (column planes, chunks
 // permuted per row against bank conflicts); the loads of
 // tile t+1 (and the indices of tile t+2) are in flight while tile t is
 // consumed.  Both contractions run on v_mfma_f32_32x32x16_bf16:
@@ -16,7 +16,8 @@
 //   O^T += V_tile^T . P^T (A = V via transposing LDS reads, B = P from the S^T
 //                          accumulators, converted to bf16)
 // so every lane owns one query row for the whole online softmax (fp32, exp2
-// with the scale folded in); the only cross-lane step is one max exchange.
+// with the scale folded in); the only cross-lane step is one max exchange
+// between the two 32-lane halves, done in the VALU.
 // The dense mode runs the very same code with contiguous key rows, so the
 // sparse/dense time ratio measures the cost of gathering alone.
 #include "mcs_common.h"
@@ -26,6 +27,7 @@ namespace mcs {
 
 // Headroom of the lazily updated running max, in log2 units.
 constexpr float kLazyLog2 = 8.0f;
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <int D, int C, int MODE>
 __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[4 * TILE];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ql = lane & 31;
   const int h = lane >> 5;
 
@@ -68,34 +70,47 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
       (MODE == ATTN_DENSE) ? nullptr : p.kv_idx + ((size_t)bh * G + g) * p.topk;
 
   // ---- gather geometry ----
-  // Copy instruction `ins` fills plane ins/4, tile rows 16*(ins%4) .. +15;
-  // lane l writes row 16*(ins%4) + l/4, physical chunk l%4, i.e. logical
-  // chunk (l%4) ^ ((l/16)%4) of that plane: columns 32*(ins/4) + 8*chunk.
-  const int grow = lane >> 2;
-  const int gcol = 8 * ((lane ^ (lane >> 4)) & 3);
-  int tok[IPW];
+  // Copy instruction `ins` (the wavefront's i-th: ins = w*IPW + i) fills
+  // plane ins/4, tile slots 16*(ins%4) .. +15; lane l writes slot
+  // 16*(ins%4) + l/4, physical chunk l%4, i.e. logical chunk (l%4)^((l/16)%4)
+  // of that plane.  Slot 16*r + j holds key 4*j + r of the tile, so a lane's
+  // copies need the consecutive keys 4*(l/4) + r0 + i (r0 = (w*IPW)%4): one
+  // offset register serves all its index loads.  Any fixed order of the keys
+  // inside a tile is valid, as K and V share it and only the final-tile mask
+  // looks at key positions.  K, V and the index row are read through buffer
+  // resources with 32-bit offsets; reads past a resource's end return zero,
+  // which the final-tile mask covers for the index row.
+  constexpr int NTOK = IPW < 4 ? IPW : 4;     // distinct keys per lane per tile
+  constexpr int RSH = (D == 128) ? 8 : 7;     // log2 of the row size in bytes
+  const int r0 = (w * IPW) & 3;
+  const int j4 = 4 * (lane >> 2);
+  const uint32_t gcb = 16u * (uint32_t)((lane ^ (lane >> 4)) & 3);
+  const uint32_t plane_soff = (uint32_t)((w * IPW) >> 2) * 64u;
+  const uint32_t mat_bytes = (uint32_t)p.n_pad << RSH;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, mat_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, mat_bytes);
+  const __amdgpu_buffer_rsrc_t irs =
+      (MODE == ATTN_DENSE) ? krs : make_rsrc(idxrow, (uint32_t)p.topk * 4u);
+  int tok[NTOK];
   auto fetch_idx = [&](int t) {
+    const int key0 = t * KT + j4 + r0;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int ins = w * IPW + i;
-      int pos = t * KT + 16 * (ins & 3) + grow;
+    for (int i = 0; i < NTOK; ++i) {
       if (MODE == ATTN_DENSE) {
-        tok[i] = pos;
+        tok[i] = key0 + i;
       } else {
-        pos = pos < nk ? pos : nk - 1;
-        tok[i] = idxrow[pos];
+        tok[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, (uint32_t)(key0 + i) * 4u, 0, 0);
       }
     }
   };
   auto issue = [&](int buf) {
-    char* kdst = lds + buf * 2 * TILE;
+    char* kdst = lds + buf * 2 * TILE + w * IPW * 1024;
     char* vdst = kdst + TILE;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int ins = w * IPW + i;
-      const size_t off = (size_t)tok[i] * D + 32 * (ins >> 2) + gcol;
-      gather16(Kb + off, kdst + ins * 1024);
-      gather16(Vb + off, vdst + ins * 1024);
+      const uint32_t voff = ((uint32_t)tok[i % NTOK] << RSH) | gcb;
+      gather16_buf(krs, kdst + i * 1024, voff, plane_soff + (i >> 2) * 64);
+      gather16_buf(vrs, vdst + i * 1024, voff, plane_soff + (i >> 2) * 64);
     }
   };
 
@@ -149,14 +164,16 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
       s1 = mfma32(a1, qreg[kk], s1);
     }
 
-    // mask keys past the end in the last tile
+    // mask keys past the end in the last tile (slot s holds key
+    // 4*(s%16) + s/16; slots s and s+32 hold keys two apart)
     if ((t + 1) * KT > nk) {
       const int lim = nk - t * KT;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = 8 * (j >> 2) + 4 * h + (j & 3);
+        const int slot = 8 * (j >> 2) + 4 * h + (j & 3);
+        const int key = 4 * (slot & 15) + (slot >> 4);
         if (key >= lim) s0[j] = -INFINITY;
-        if (key + 32 >= lim) s1[j] = -INFINITY;
+        if (key + 2 >= lim) s1[j] = -INFINITY;
       }
     }
 
@@ -170,7 +187,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
     for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s0[j]);
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s1[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(mx);
     const bool raise = (mx - mrun) * c2 > kLazyLog2;
     if (__any(raise)) {
       const float mnew = raise ? mx : mrun;
@@ -183,17 +200,29 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
         for (int j = 0; j < 16; ++j) o[T][j] *= alpha;
     }
     const float mc = mrun * c2;
-    float ls = 0.f;
     bf16x8 pb[4];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[j], c2, -mc));
       const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[j], c2, -mc));
-      ls += e0 + e1;
       pb[j >> 3][j & 7] = (__bf16)e0;
       pb[2 + (j >> 3)][j & 7] = (__bf16)e1;
     }
-    lrun += ls;
+    // row sum of the bf16 probabilities the PV product uses (so numerator and
+    // denominator see the same rounded weights), two per dot2 instruction
+    {
+      float la = 0.f, lb = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2 p01 = {pb[q][0], pb[q][1]}, p23 = {pb[q][2], pb[q][3]};
+        const bf16x2 p45 = {pb[q][4], pb[q][5]}, p67 = {pb[q][6], pb[q][7]};
+        la = __builtin_amdgcn_fdot2_f32_bf16(p01, kOnes2, la, false);
+        lb = __builtin_amdgcn_fdot2_f32_bf16(p23, kOnes2, lb, false);
+        la = __builtin_amdgcn_fdot2_f32_bf16(p45, kOnes2, la, false);
+        lb = __builtin_amdgcn_fdot2_f32_bf16(p67, kOnes2, lb, false);
+      }
+      lrun += la + lb;
+    }
 
     // O^T += V^T . P^T.  The transposing reads are issued from inline asm
     // (with their wait inside the same block) so that the compiler does not
@@ -213,7 +242,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   }
 
   // ---- epilogue ----
-  const float lsum = lrun + __shfl_xor(lrun, 32);
+  const float lsum = sum_xor32(lrun);
   const float inv = 1.f / lsum;
   const bool valid = qrow < p.n_valid;
   uint16_t* Ob = p.out + mat + (size_t)qrow * D;

@@ -51,8 +51,8 @@ int32_t check_dims(const mcs_dims* d) {
     return fail(MCS_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
   if (d->group_size != 64 && d->group_size != 128)
     return fail(MCS_ERR_UNSUPPORTED, "group_size %d not supported (64 or 128)", d->group_size);
-  if (d->n_pad < 1 || d->n_pad > (1 << 24))
-    return fail(MCS_ERR_UNSUPPORTED, "n_pad %d outside 1 .. 2^24", d->n_pad);
+  if (d->n_pad < 1 || d->n_pad >= (1 << 24))
+    return fail(MCS_ERR_UNSUPPORTED, "n_pad %d outside 1 .. 2^24 - 1", d->n_pad);
   if (d->n_pad % d->group_size != 0)
     return fail(MCS_ERR_INVALID_ARG, "n_pad %d is not a multiple of group_size %d", d->n_pad,
                 d->group_size);

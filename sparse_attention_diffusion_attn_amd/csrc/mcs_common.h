@@ -8,6 +8,7 @@ namespace mcs {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -36,9 +37,30 @@ __device__ __forceinline__ int plane_chunk(int row, int chunk4) {
   return (chunk4 ^ (row >> 2)) & 3;
 }
 
-// Per-lane 16-byte global -> LDS copy; lane l's bytes land at lds_base + 16*l.
-__device__ __forceinline__ void gather16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+// Raw buffer resource over `bytes` bytes at `base` (stride 0; loads past the
+// end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Per-lane 16-byte buffer -> LDS copy from byte offset voff + soff (soff
+// uniform) of the resource; lane l's bytes land at lds_base + 16*l (lds_base
+// uniform).
+__device__ __forceinline__ void gather16_buf(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff,
+                                             uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+}
+
+// Max / sum of this lane's value and lane (l ^ 32)'s, exchanged in the VALU
+// (v_permlane32_swap swaps the two 32-lane halves; the pair it returns is
+// {x[l], x[l^32]} in an order that a symmetric operation does not see).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

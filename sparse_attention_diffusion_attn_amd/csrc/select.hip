@@ -32,10 +32,10 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
   constexpr int KS = D / 16;
 
   __shared__ __attribute__((aligned(1024))) char lds[2 * TILE];
-  __shared__ float red[NW][KT];
+  __shared__ float red[2][NW][KT];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ql = lane & 31;
   const int h = lane >> 5;
 
@@ -67,15 +67,21 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
 
   const int nk = p.n_valid;
   const int ntiles = (nk + KT - 1) / KT;
-  const int grow = lane >> 2;
-  const int gcol = 8 * ((lane ^ (lane >> 4)) & 3);
+  // Copy instruction ins = w*IPW + i fills plane ins/4, rows 16*(ins%4) + l/4
+  // (lane l), physical chunk l%4 = logical chunk (l%4)^((l/16)%4); rows are
+  // read through a buffer resource with 32-bit offsets, the per-instruction
+  // part of the offset in a scalar register.
+  constexpr int RSH = (D == 128) ? 8 : 7;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, (uint32_t)p.n_pad << RSH);
+  const uint32_t lane_off = ((uint32_t)(lane >> 2) << RSH) | (16u * (uint32_t)((lane ^ (lane >> 4)) & 3));
   auto issue = [&](int t, int buf) {
-    char* kdst = lds + buf * TILE;
+    char* kdst = lds + buf * TILE + w * IPW * 1024;
+    const uint32_t voff = ((uint32_t)(t * KT) << RSH) + lane_off;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int ins = w * IPW + i;
-      const int row = t * KT + 16 * (ins & 3) + grow;
-      gather16(Kb + (size_t)row * D + 32 * (ins >> 2) + gcol, kdst + ins * 1024);
+      const uint32_t soff = ((uint32_t)(16 * (ins & 3)) << RSH) + 64u * (uint32_t)(ins >> 2);
+      gather16_buf(krs, kdst + i * 1024, voff, soff);
     }
   };
   const int sq = (ql >> 2) & 3;
@@ -84,10 +90,24 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
   const float c2 = p.scale * kLog2e;
   float* out = p.scores + ((size_t)bl * G + g) * (size_t)nk;
 
+  // Column sums of tile t are finished (fixed wavefront order) by the first
+  // KT threads after the barrier at the top of tile t+1; the partials are
+  // double-buffered so one barrier per tile suffices.
+  auto finish = [&](int t) {
+    if (threadIdx.x < KT) {
+      const int key = t * KT + threadIdx.x;
+      float a = red[t & 1][0][threadIdx.x];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) a += red[t & 1][ww][threadIdx.x];
+      if (key < nk) out[key] = a;
+    }
+  };
+
   issue(0, 0);
   for (int t = 0; t < ntiles; ++t) {
     wait_vm0();
     __syncthreads();
+    if (t > 0) finish(t - 1);
     if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
     const char* kbuf = lds + (t & 1) * TILE;
     f32x16 s0, s1;
@@ -107,21 +127,15 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
       a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(s0[j], c2, -lse2[j]));
       a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(s1[j], c2, -lse2[j]));
     }
-    a0 += __shfl_xor(a0, 32);
-    a1 += __shfl_xor(a1, 32);
+    a0 = sum_xor32(a0);
+    a1 = sum_xor32(a1);
     if (h == 0) {
-      red[w][ql] = a0;
-      red[w][32 + ql] = a1;
-    }
-    __syncthreads();
-    if (threadIdx.x < KT) {
-      const int key = t * KT + threadIdx.x;
-      float a = red[0][threadIdx.x];
-#pragma unroll
-      for (int ww = 1; ww < NW; ++ww) a += red[ww][threadIdx.x];
-      if (key < nk) out[key] = a;
+      red[t & 1][w][ql] = a0;
+      red[t & 1][w][32 + ql] = a1;
     }
   }
+  __syncthreads();
+  finish(ntiles - 1);
 }
 
 // ---------------------------------------------------------------------------
