@@ -9,9 +9,10 @@
 // One workgroup per (head, query group): C/32 wavefronts, each owning 32 query
 // rows.  Key/value tiles of 64 rows are gathered by index with 16-byte
 // buffer->LDS copies into a double-buffered LDS tile (column planes, chunks
-// permuted per row against bank conflicts); the loads of
-// tile t+1 (and the indices of tile t+2) are in flight while tile t is
-// consumed.  Both contractions run on v_mfma_f32_32x32x16_bf16:
+// permuted per row against bank conflicts).  The copies of tile t+1 are
+// issued one per k-step of tile t's QK^T product (spread out, so the vector
+// memory queues never fill in a burst) and the indices of tile t+2 after it;
+// both are in flight while tile t is consumed.  Both contractions run on v_mfma_f32_32x32x16_bf16:
 //   S^T = K_tile . Q^T   (A = gathered K rows from LDS, B = Q held in VGPRs)
 //   O^T += V_tile^T . P^T (A = V via transposing LDS reads, B = P from the S^T
 //                          accumulators, converted to bf16)
@@ -144,25 +145,47 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   for (int t = 0; t < ntiles; ++t) {
     wait_vm0();
     __syncthreads();
-    if (t + 1 < ntiles) {
-      issue((t + 1) & 1);
-      if (t + 2 < ntiles) fetch_idx(t + 2);
-    }
+    const bool more = t + 1 < ntiles;
+    char* kdst_n = lds + ((t + 1) & 1) * 2 * TILE + w * IPW * 1024;
     const char* kbuf = lds + (t & 1) * 2 * TILE;
     const char* vbuf = kbuf + TILE;
 
-    // S^T = K . Q^T for the 64 keys of this tile (two 32-key blocks)
+    // S^T = K . Q^T for the 64 keys of this tile (two 32-key blocks).  The K
+    // operands of k-step kk+1 are read while the products of kk run, and
+    // step kk also issues its share of tile t+1's copies.
     f32x16 s0, s1;
 #pragma unroll
     for (int j = 0; j < 16; ++j) { s0[j] = 0.f; s1[j] = 0.f; }
+    bf16x8 a0 = *(const bf16x8*)(kbuf + koff_e);
+    bf16x8 a1 = *(const bf16x8*)(kbuf + koff_e + 2048);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const char* kp = kbuf + ((kk & 1) ? koff_o : koff_e) + (kk >> 1) * 4096;
-      const bf16x8 a0 = *(const bf16x8*)(kp);
-      const bf16x8 a1 = *(const bf16x8*)(kp + 2048);
+      bf16x8 n0 = a0, n1 = a1;
+      if (kk + 1 < KS) {
+        const char* kp = kbuf + (((kk + 1) & 1) ? koff_o : koff_e) + ((kk + 1) >> 1) * 4096;
+        n0 = *(const bf16x8*)(kp);
+        n1 = *(const bf16x8*)(kp + 2048);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       s0 = mfma32(a0, qreg[kk], s0);
       s1 = mfma32(a1, qreg[kk], s1);
+      a0 = n0;
+      a1 = n1;
+      if (more) {
+        constexpr int PER = (2 * IPW + KS - 1) / KS;
+#pragma unroll
+        for (int c = kk * PER; c < (kk + 1) * PER && c < 2 * IPW; ++c) {
+          const int i = c >> 1;
+          const uint32_t voff = ((uint32_t)tok[i % NTOK] << RSH) | gcb;
+          if (c & 1)
+            gather16_buf(vrs, kdst_n + TILE + i * 1024, voff, plane_soff + (i >> 2) * 64);
+          else
+            gather16_buf(krs, kdst_n + i * 1024, voff, plane_soff + (i >> 2) * 64);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (t + 2 < ntiles) fetch_idx(t + 2);
 
     // mask keys past the end in the last tile (slot s holds key
     // 4*(s%16) + s/16; slots s and s+32 hold keys two apart)

@@ -108,7 +108,10 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
     wait_vm0();
     __syncthreads();
     if (t > 0) finish(t - 1);
-    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+    // the copies of tile t+1 are spread over the k-steps of tile t
+    const bool more = t + 1 < ntiles;
+    char* kdst_n = lds + ((t + 1) & 1) * TILE + w * IPW * 1024;
+    const uint32_t voff_n = ((uint32_t)((t + 1) * KT) << RSH) + lane_off;
     const char* kbuf = lds + (t & 1) * TILE;
     f32x16 s0, s1;
 #pragma unroll
@@ -120,6 +123,16 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
       const bf16x8 b1 = *(const bf16x8*)(kp + 2048);
       s0 = mfma32(qreg[kk], b0, s0);
       s1 = mfma32(qreg[kk], b1, s1);
+      if (more) {
+        constexpr int PER = (IPW + KS - 1) / KS;
+#pragma unroll
+        for (int i = kk * PER; i < (kk + 1) * PER && i < IPW; ++i) {
+          const int ins = w * IPW + i;
+          const uint32_t soff = ((uint32_t)(16 * (ins & 3)) << RSH) + 64u * (uint32_t)(ins >> 2);
+          gather16_buf(krs, kdst_n + i * 1024, voff_n, soff);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
