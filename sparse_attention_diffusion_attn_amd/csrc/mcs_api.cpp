@@ -192,9 +192,11 @@ int32_t mcs_group(const mcs_dims* dims, const uint16_t* q, int32_t power_iters,
     MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 0, p, s), "pddp mean"));
     MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 0, p, s), "pddp mean reduce"));
     for (int it = 0; it < power_iters; ++it) {
+      p.fix_sign = (it == power_iters - 1) ? 1 : 0;
       MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 1, p, s), "pddp power step"));
       MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 1, p, s), "pddp power reduce"));
     }
+    p.fix_sign = 0;
     MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 2, p, s), "pddp projection"));
     MCS_TRY(hip_status(mcs::launch_pddp_split(c, p, s), "pddp split"));
     cur = 1 - cur;

@@ -51,6 +51,7 @@ struct PddpParams {
   double* proj;           // [BH, n_pad] by position
   int64_t bh;
   int32_t n_pad, groups, level;
+  int32_t fix_sign;       // reduce stage 1: apply the sign rule to v (last power step)
 };
 
 hipError_t launch_attention(int mode, int head_dim, int group_size, const AttnParams& p,
@@ -63,6 +64,7 @@ hipError_t launch_pddp_identity(const PddpParams& p, hipStream_t s);
 hipError_t launch_pddp_partial(int head_dim, int group_size, int stage, const PddpParams& p,
                                hipStream_t s);
 // stage: 0 = finish means and set v0, 1 = finish a power-iteration step
+// (and, with p.fix_sign, make v's largest-magnitude component positive)
 hipError_t launch_pddp_reduce(int head_dim, int group_size, int stage, const PddpParams& p,
                               hipStream_t s);
 hipError_t launch_pddp_split(int group_size, const PddpParams& p, hipStream_t s);

@@ -63,65 +63,114 @@ __global__ void pddp_identity_kernel(int32_t* perm, int n_pad, int64_t total) {
   if (i < total) perm[i] = (int32_t)(i % n_pad);
 }
 
+// fp64 value of another lane, moved by a DPP lane pattern (both 32-bit halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Sum over aligned groups of N = 8 or 16 lanes, the same bits in every lane of
+// a group: pairs (quad_perm 1,0,3,2), quads (quad_perm 2,3,0,1), halves of a
+// 16-lane row (row_half_mirror), whole rows (row_mirror).  Each step adds a
+// lane's value to its partner's in the other half of the block being merged,
+// and the partner adds the same two numbers, so every lane ends with
+// bitwise the same sum.
+template <int N>
+__device__ __forceinline__ double group_sum(double x) {
+  x += dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f64<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f64<0x141>(x);  // row_half_mirror
+  if (N == 16) x += dpp_f64<0x140>(x);  // row_mirror
+  return x;
+}
+// x + (value of lane l ^ 16) and x + (value of lane l ^ 32), in the VALU.
+__device__ __forceinline__ double add_xor16(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  const double a = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0]));
+  const double b = __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+  return a + b;
+}
+__device__ __forceinline__ double add_xor32(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  const double a = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0]));
+  const double b = __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+  return a + b;
+}
+
 // stage 0: partial[g] = sum of the block's rows
 // stage 1: partial[g] = sum_r ((x_r - mu) . v) (x_r - mu)
-// stage 2: proj[pos] = (x_r - mu) . v', v' = v with its sign fixed
+// stage 2: proj[pos] = (x_r - mu) . v (v with its sign already fixed)
+//
+// Persistent: workgroup i handles the C-row blocks i, i + P, i + 2P, ... (P =
+// grid size, all resident), each block being one group of perm (block b =
+// head b / G, group b % G).  Thread (dg, rg) owns dimensions 8dg .. 8dg+7 of
+// the rows rg, rg + RG, ... of a block and keeps them in VGPRs (bf16); the DG
+// threads of a row are consecutive lanes.  While block b is computed, the rows
+// of block b + P (and the perm indices of block b + 2P) are loading, and the
+// node's mu / v of block b + P are copied into the other half of a
+// double-buffered LDS pair, so the workgroup never waits on a dependent load
+// chain.  Reductions: per-row dot products over the DG lanes of the row with
+// DPP moves; per-dimension sums over a wavefront's row groups with lane swaps,
+// then over the four wavefronts in LDS (fixed orders throughout).
+//
+// Arithmetic (fp64): with c = mu . v,
+//   t_r = (x_r - mu) . v = x_r . v - c
+//   sum_r t_r (x_r - mu) = sum_r t_r x_r - mu sum_r t_r
+// (the same sums, regrouped so that every element costs one FMA per pass).
 template <int D, int C, int STAGE>
 __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   constexpr int NT = 256;
-  // thread (dg, rg) works on dimensions 8dg .. 8dg+7 of rows rg, rg+RG, ...
   constexpr int DG = D / 8, RG = NT / DG, RPT = C / RG;
-  constexpr int TP = DG + 1;  // padded row of per-row partial dot products
-  __shared__ __attribute__((aligned(16))) uint16_t xs[C * D];
-  __shared__ double mus[D], vs[D];
-  __shared__ double ts[C];
-  __shared__ double part[(C * TP > RG * D) ? C * TP : RG * D];
-  __shared__ int flip;
+  static_assert(DG == 8 || DG == 16, "row lanes");
+  __shared__ __attribute__((aligned(16))) double muv[2][2][128];  // [buf][mu | v][d]
+  __shared__ double part[NT / 64][D];
 
   const int G = p.groups;
-  const int work = blockIdx.x;
-  const int64_t bh = work / G;
-  const int g = work - (int)(bh * G);
-  int s, m;
-  node_of(G, p.level, g, s, m);
-  if (m < 2) return;
+  const int64_t nblk = p.bh * (int64_t)G;
+  const int64_t P = gridDim.x;
   const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int dg = tid % DG, rg = tid / DG;
-  const int32_t* pc = p.perm_cur + (size_t)bh * p.n_pad + (size_t)g * C;
-  const uint16_t* Qb = p.q + (size_t)bh * p.n_pad * D;
 
-  // stage the block's C rows (bf16) in LDS: all row indices first, then all
-  // 16-byte loads, then the LDS stores (one round trip for each)
-  {
-    constexpr int NL = C * D / 8 / NT;
-    int rows[NL];
-#pragma unroll
-    for (int k = 0; k < NL; ++k) rows[k] = pc[(tid + k * NT) / (D / 8)];
-    uint4 vals[NL];
-#pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      const int c8 = (tid + k * NT) % (D / 8);
-      vals[k] = *(const uint4*)(Qb + (size_t)rows[k] * D + c8 * 8);
-    }
-#pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      const int e = tid + k * NT;
-      *(uint4*)(xs + (e / (D / 8)) * D + (e % (D / 8)) * 8) = vals[k];
-    }
-  }
-  if (STAGE > 0) {
-    const double* mu = p.mu + ((size_t)bh * G + s) * D;
-    const double* vv = p.vec + ((size_t)bh * G + s) * D;
-    for (int d = tid; d < D; d += NT) {
-      mus[d] = mu[d];
-      vs[d] = vv[d];
-    }
-  }
-  __syncthreads();
+  const __amdgpu_buffer_rsrc_t murs =
+      make_rsrc(p.mu, (uint32_t)min<int64_t>(nblk * D * 8, 0xffffffffll));
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc(p.vec, (uint32_t)min<int64_t>(nblk * D * 8, 0xffffffffll));
 
-  // eight bf16 of row r, dimensions 8dg .. 8dg+7, as doubles
-  auto row8 = [&](int r, double (&x)[8]) {
-    const uint4 xv = *(const uint4*)(xs + r * D + 8 * dg);
+  // perm indices of this thread's rows in block b
+  auto load_idx = [&](int64_t b, int (&ix)[RPT]) {
+    const int64_t bh = b / G;
+    const int g = (int)(b - bh * G);
+    const int32_t* pc = p.perm_cur + bh * p.n_pad + (int64_t)g * C;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) ix[k] = pc[rg + k * RG];
+  };
+  // this thread's 8 bf16 of each of its rows (16 bytes each)
+  auto load_rows = [&](int64_t b, const int (&ix)[RPT], uint4 (&xr)[RPT]) {
+    const int64_t bh = b / G;
+    const uint16_t* Qb = p.q + bh * p.n_pad * D;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) xr[k] = *(const uint4*)(Qb + (int64_t)ix[k] * D + 8 * dg);
+  };
+  // mu and v of block b's node into LDS half `buf` (one 16-byte copy per lane
+  // of waves 0 and 1; for D = 64 the upper half of the copy is not used)
+  auto load_muv = [&](int64_t b, int buf) {
+    if (STAGE == 0 || w > 1) return;
+    const int64_t bh = b / G;
+    int s, m;
+    node_of(G, p.level, (int)(b - bh * G), s, m);
+    const uint32_t off = (uint32_t)(((bh * G + s) * D) * 8) + 16u * (uint32_t)lane;
+    if (w == 0) gather16_buf(murs, &muv[buf][0][0], off, 0);
+    else gather16_buf(vrs, &muv[buf][1][0], off, 0);
+  };
+  auto to_f64 = [&](const uint4& xv, double (&x)[8]) {
     const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -129,110 +178,137 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
       x[2 * e + 1] = (double)__uint_as_float(w4[e] & 0xffff0000u);
     }
   };
-  // column partials part[rg][d] -> fixed-order sum over rg, for d = tid < D
-  auto column_total = [&]() {
-    double tot = 0.0;
-    if (tid < D) {
-      tot = part[tid];
-      for (int q = 1; q < RG; ++q) tot += part[q * D + tid];
+  // per-dimension block totals: acc[e] (dimension 8dg+e, this thread's rows)
+  // summed over the wavefront's row groups, then over the wavefronts in order
+  auto store_totals = [&](int64_t bh, int g, double (&acc)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double x = acc[e];
+      if (DG == 8) x += dpp_f64<0x128>(x);  // row_ror:8 = lane ^ 8 inside a 16-lane row
+      x = add_xor16(x);
+      x = add_xor32(x);
+      acc[e] = x;
     }
-    return tot;
+    if (lane < DG) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[w][8 * dg + e] = acc[e];
+    }
+    __syncthreads();
+    if (tid < D) {
+      double tot = part[0][tid];
+#pragma unroll
+      for (int q = 1; q < NT / 64; ++q) tot += part[q][tid];
+      p.partial[((size_t)bh * G + g) * D + tid] = tot;
+    }
   };
 
-  if (STAGE == 0) {
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-      double x[8];
-      row8(rg + k * RG, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += x[e];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[rg * D + 8 * dg + e] = acc[e];
-    __syncthreads();
-    const double tot = column_total();
-    if (tid < D) p.partial[((size_t)bh * G + g) * D + tid] = tot;
-    return;
-  }
+  int64_t b = blockIdx.x;
+  if (b >= nblk) return;
+  int idx_n[RPT];
+  uint4 xr[RPT], xr_n[RPT];
+  load_idx(b, idx_n);
+  wait_vm0();
+  load_rows(b, idx_n, xr);
+  load_muv(b, 0);
+  if (b + P < nblk) load_idx(b + P, idx_n);
 
-  if (STAGE == 2) {
-    if (tid == 0) {
-      int best = 0;
-      double bv = fabs(vs[0]);
-      for (int d = 1; d < D; ++d) {
-        const double a = fabs(vs[d]);
-        if (a > bv) { bv = a; best = d; }
+  for (int it = 0; b < nblk; ++it, b += P) {
+    wait_vm0();
+    __syncthreads();
+    const int buf = it & 1;
+    // prefetch block b + P (rows, mu / v) and the indices of block b + 2P
+    if (b + P < nblk) {
+      load_rows(b + P, idx_n, xr_n);
+      load_muv(b + P, buf ^ 1);
+      if (b + 2 * P < nblk) load_idx(b + 2 * P, idx_n);
+    }
+    const int64_t bh = b / G;
+    const int g = (int)(b - bh * G);
+    int s, m;
+    node_of(G, p.level, g, s, m);
+    if (m >= 2) {
+      double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (STAGE == 0) {
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+          double x[8];
+          to_f64(xr[k], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += x[e];
+        }
+        store_totals(bh, g, acc);
+      } else {
+        double mu8[8], v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mu8[e] = muv[buf][0][8 * dg + e];
+          v8[e] = muv[buf][1][8 * dg + e];
+        }
+        double c = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c = __builtin_fma(mu8[e], v8[e], c);
+        // t_r = x_r . v - c summed over the DG lanes of row r
+        double t[RPT];
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+          double x[8];
+          to_f64(xr[k], x);
+          double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            a0 = __builtin_fma(x[e], v8[e], a0);
+            a1 = __builtin_fma(x[e + 1], v8[e + 1], a1);
+          }
+          t[k] = group_sum<DG>((a0 + a1) - c);
+        }
+        if (STAGE == 2) {
+          if (dg == 0) {
+            double* pr = p.proj + (size_t)bh * p.n_pad + (size_t)g * C;
+#pragma unroll
+            for (int k = 0; k < RPT; ++k) pr[rg + k * RG] = t[k];
+          }
+        } else {
+          // w_d = sum_r t_r x_rd - mu_d sum_r t_r over this thread's rows (the
+          // rows are converted again: keeping all of them as doubles would
+          // take 4*RPT more VGPRs than the bf16 copies)
+#pragma unroll
+          for (int k = 0; k < RPT; ++k)
+            asm volatile("" : "+v"(xr[k].x), "+v"(xr[k].y), "+v"(xr[k].z), "+v"(xr[k].w));
+          double tsum = 0.0;
+#pragma unroll
+          for (int k = 0; k < RPT; ++k) {
+            tsum += t[k];
+            double x[8];
+            to_f64(xr[k], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(t[k], x[e], acc[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(-mu8[e], tsum, acc[e]);
+          store_totals(bh, g, acc);
+        }
       }
-      flip = vs[best] < 0.0 ? 1 : 0;
-    }
-    __syncthreads();
-    if (flip) {
-      for (int d = tid; d < D; d += NT) vs[d] = -vs[d];
-    }
-    __syncthreads();
-  }
-
-  double mu8[8], v8[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    mu8[e] = mus[8 * dg + e];
-    v8[e] = vs[8 * dg + e];
-  }
-  // t_r = (x_r - mu) . v: partial dot products over each thread's 8
-  // dimensions, then a fixed-order sum over the DG partials of each row
-#pragma unroll
-  for (int k = 0; k < RPT; ++k) {
-    const int r = rg + k * RG;
-    double x[8];
-    row8(r, x);
-    double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      a0 = __builtin_fma(x[e] - mu8[e], v8[e], a0);
-      a1 = __builtin_fma(x[e + 1] - mu8[e + 1], v8[e + 1], a1);
-    }
-    part[r * TP + dg] = a0 + a1;
-  }
-  __syncthreads();
-  if (tid < C) {
-    double t = part[tid * TP];
-    for (int q = 1; q < DG; ++q) t += part[tid * TP + q];
-    ts[tid] = t;
-  }
-  __syncthreads();
-  if (STAGE == 2) {
-    if (tid < C) p.proj[(size_t)bh * p.n_pad + (size_t)g * C + tid] = ts[tid];
-    return;
-  }
-  // w_d = sum_r t_r (x_rd - mu_d)
-  {
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-      const int r = rg + k * RG;
-      const double t = ts[r];
-      double x[8];
-      row8(r, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(t, x[e] - mu8[e], acc[e]);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) part[rg * D + 8 * dg + e] = acc[e];
-    __syncthreads();
-    const double tot = column_total();
-    if (tid < D) p.partial[((size_t)bh * G + g) * D + tid] = tot;
+    for (int k = 0; k < RPT; ++k) xr[k] = xr_n[k];
   }
 }
 
 // stage 0: mu = (sum of partials) / rows, v = v0 = 1/sqrt(D)
-// stage 1: w = sum of partials; v = w / |w| if |w| > 0
-template <int D, int C, int STAGE>
-__global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
-  constexpr int NT = 256;
-  constexpr int PARTS = NT / D;
+// stage 1: w = sum of partials; v = w / |w| if |w| > 0; after the last power
+//          step (p.fix_sign) the component of largest magnitude (first on
+//          ties) is made positive.
+// One workgroup of D*PARTS threads per node (PARTS chosen per depth from the
+// largest node size): thread (d, part) sums the partials of groups s + part,
+// s + part + PARTS, ... in that order (independent loads, one dependent add
+// chain), then the PARTS sums of each d in order.
+template <int D, int C, int STAGE, int PARTS>
+__global__ __launch_bounds__(D * PARTS) void pddp_reduce_kernel(PddpParams p) {
+  constexpr int NT = D * PARTS;
   __shared__ double part_sum[NT];
   __shared__ double sq[NT];
+  __shared__ double vmag[D];
+  __shared__ int vidx[D];
   const int G = p.groups;
   const int slots = 1 << p.level;
   const int64_t bh = blockIdx.x / slots;
@@ -240,9 +316,17 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
   if (!node_of_slot(G, p.level, blockIdx.x - (int)(bh * slots), s, m) || m < 2) return;
   const int tid = threadIdx.x;
   const int d = tid % D, part = tid / D;
-  // groups s + part, s + part + PARTS, ... in order
+  const double* src = p.partial + ((size_t)bh * G + s) * D + d;
   double acc = 0.0;
-  for (int gg = s + part; gg < s + m; gg += PARTS) acc += p.partial[((size_t)bh * G + gg) * D + d];
+  int gg = part;
+  for (; gg + 15 * PARTS < m; gg += 16 * PARTS) {
+    double a[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) a[u] = src[(size_t)(gg + u * PARTS) * D];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc += a[u];
+  }
+  for (; gg < m; gg += PARTS) acc += src[(size_t)gg * D];
   part_sum[tid] = acc;
   __syncthreads();
   double tot = 0.0;
@@ -266,7 +350,30 @@ __global__ __launch_bounds__(256) void pddp_reduce_kernel(PddpParams p) {
     __syncthreads();
   }
   const double nrm2 = sq[0];
-  if (tid < D && nrm2 > 0.0) vv[tid] = tot / sqrt(nrm2);
+  double nv = 0.0;
+  if (tid < D) nv = (nrm2 > 0.0) ? tot / sqrt(nrm2) : vv[tid];
+  if (p.fix_sign) {
+    if (tid < D) {
+      vmag[tid] = fabs(nv);
+      vidx[tid] = tid;
+    }
+    __syncthreads();
+    for (int o = D / 2; o > 0; o >>= 1) {
+      if (tid < o) {
+        const double a = vmag[tid], b = vmag[tid + o];
+        const int ia = vidx[tid], ib = vidx[tid + o];
+        if (b > a || (b == a && ib < ia)) {
+          vmag[tid] = b;
+          vidx[tid] = ib;
+        }
+      }
+      __syncthreads();
+    }
+    if (tid == vidx[0]) sq[0] = nv;   // the signed value of the largest component
+    __syncthreads();
+    if (sq[0] < 0.0) nv = -nv;
+  }
+  if (tid < D) vv[tid] = nv;
 }
 
 template <int NT>
@@ -423,13 +530,35 @@ hipError_t launch_pddp_identity(const PddpParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Grid of a persistent kernel: as many workgroups as are resident at once on
+// the current device (at most `work`).
+template <typename K>
+static unsigned resident_grid(K kernel, int threads, int64_t work) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      cus < 1 || per_cu < 1) {
+    cus = 1;
+    per_cu = 1;
+  }
+  const int64_t r = (int64_t)cus * per_cu;
+  return (unsigned)(work < r ? work : r);
+}
+
+template <int D, int C, int STAGE>
+static hipError_t partial_one(const PddpParams& p, hipStream_t s) {
+  const int64_t work = p.bh * (int64_t)p.groups;
+  const unsigned grid = resident_grid(pddp_partial_kernel<D, C, STAGE>, 256, work);
+  hipLaunchKernelGGL((pddp_partial_kernel<D, C, STAGE>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D, int C>
 static hipError_t partial_t(int stage, const PddpParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.bh * p.groups));
-  if (stage == 0) hipLaunchKernelGGL((pddp_partial_kernel<D, C, 0>), grid, dim3(256), 0, s, p);
-  else if (stage == 1) hipLaunchKernelGGL((pddp_partial_kernel<D, C, 1>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((pddp_partial_kernel<D, C, 2>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  if (stage == 0) return partial_one<D, C, 0>(p, s);
+  if (stage == 1) return partial_one<D, C, 1>(p, s);
+  return partial_one<D, C, 2>(p, s);
 }
 
 hipError_t launch_pddp_partial(int d, int c, int stage, const PddpParams& p, hipStream_t s) {
@@ -440,11 +569,28 @@ hipError_t launch_pddp_partial(int d, int c, int stage, const PddpParams& p, hip
   return hipErrorInvalidValue;
 }
 
+template <int D, int C, int PARTS>
+static void reduce_one(int stage, const PddpParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)(p.bh << p.level));
+  if (stage == 0) hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 0, PARTS>), grid, dim3(D * PARTS), 0, s, p);
+  else hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 1, PARTS>), grid, dim3(D * PARTS), 0, s, p);
+}
+
 template <int D, int C>
 static hipError_t reduce_t(int stage, const PddpParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.bh << p.level));
-  if (stage == 0) hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 0>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 1>), grid, dim3(256), 0, s, p);
+  // about 8 partials per thread for the largest node of this depth
+  const int m_max = (p.groups + (1 << p.level) - 1) >> p.level;
+  int parts = 1;
+  while (parts < 1024 / D && parts * 8 < m_max) parts *= 2;
+  switch (parts) {
+    case 1: reduce_one<D, C, 1>(stage, p, s); break;
+    case 2: reduce_one<D, C, 2>(stage, p, s); break;
+    case 4: reduce_one<D, C, 4>(stage, p, s); break;
+    case 8: reduce_one<D, C, 8>(stage, p, s); break;
+    default:
+      if constexpr (D * 16 <= 1024) reduce_one<D, C, 16>(stage, p, s);
+      else reduce_one<D, C, 8>(stage, p, s);
+  }
   return hipGetLastError();
 }
 
