@@ -19,6 +19,8 @@
  *   reuse : mcs_sparse_attn
  *   mcs_dense_attn is the in-house dense kernel (anchor pass 1, and the
  *   denominator of the sparse kernel's speed-up).
+ *   Selection variants of the pages' oracle analysis: mcs_block_select, then
+ *   mcs_residual_counts / mcs_sparse_attn_counts on the block rows it writes.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -168,6 +170,56 @@ int32_t mcs_sparse_attn(const mcs_dims* dims, const uint16_t* q, const uint16_t*
 int32_t mcs_dense_attn(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, float scale, uint16_t* o, float* lse,
                        void* stream);
+
+/*
+ * Selection variants of the oracle analysis (onedev.kr summary, "how it
+ * works"): at one attention density, a block oracle picks whole KV blocks per
+ * query group with exact dense probabilities, and vanilla block-sparse
+ * attention (BSA) ranks the blocks by mean-pooled queries and keys.  KV block
+ * b holds the `block` consecutive valid keys b*block .. (the last block may be
+ * shorter).  Per group, the `nblocks` best blocks (higher score first, ties to
+ * the lower block index) are expanded to their tokens, ascending, in a row of
+ * nblocks*block entries of kv_idx; kv_count[g] is the number of tokens written
+ * and the rest of the row is set to -1.
+ *   mode MCS_BLOCK_EXACT    score(g, b) = sum over the block's keys of the
+ *                           group's exact score a_g[j] (as in
+ *                           mcs_anchor_select; needs lse from the dense pass)
+ *   mode MCS_BLOCK_MEANPOOL score(g, b) = scale * mean(q of g's valid members)
+ *                           . mean(k of block b); lse is not read (NULL ok)
+ * Query groups are those of perm: the identity partition (token blocks of C)
+ * gives the pages' query blocks, a PDDP partition the grouped variant.
+ * Scores are accumulated in fp64 and ranked in fp32.
+ *   block   : 1 .. n_valid;  nblocks : 1 .. min(1024, ceil(n_valid/block))
+ *   kv_idx  : out, int32 [B,H,G,nblocks*block];  kv_count : out, int32 [B,H,G]
+ *   workspace: mcs_block_select_workspace_bytes(...) for all heads at once;
+ *           any size >= mcs_block_select_min_workspace_bytes(...) works.
+ */
+#define MCS_BLOCK_EXACT 0
+#define MCS_BLOCK_MEANPOOL 1
+size_t mcs_block_select_workspace_bytes(const mcs_dims* dims, int32_t mode, int32_t block,
+                                        int32_t nblocks);
+size_t mcs_block_select_min_workspace_bytes(const mcs_dims* dims, int32_t mode, int32_t block,
+                                            int32_t nblocks);
+int32_t mcs_block_select(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                         const int32_t* perm, const float* lse, int32_t mode, int32_t block,
+                         int32_t nblocks, float scale, int32_t* kv_idx, int32_t* kv_count,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mcs_sparse_attn_counts / mcs_residual_counts — mcs_sparse_attn and
+ * mcs_residual for index rows of stride kv_stride whose group g uses its first
+ * kv_count[g] entries (counts outside 1 .. kv_stride are clamped into it).
+ * Everything else is as in the fixed-count calls.
+ *   kv_idx : int32 [B,H,G,kv_stride];  kv_count : int32 [B,H,G]
+ */
+int32_t mcs_sparse_attn_counts(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                               int32_t kv_stride, const int32_t* kv_count, float scale,
+                               const uint16_t* r, uint16_t* o, void* stream);
+int32_t mcs_residual_counts(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                            int32_t kv_stride, const int32_t* kv_count, float scale,
+                            const uint16_t* o_full, uint16_t* r, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,9 @@ call raises.
 Anchor step:  perm = group(q, ...);  o_full, lse, kv_idx = anchor_select(...);
               r = residual(...)
 Reuse step:   o = sparse_attn(q_t, k_t, v_t, perm, kv_idx, r, ...)
+Selection variants of the oracle analysis (block oracle, vanilla BSA):
+              kv_idx, kv_count = block_select(...);  r = residual_counts(...);
+              o = sparse_attn_counts(...)
 """
 from __future__ import annotations
 
@@ -25,6 +28,7 @@ LIB_PATH = os.path.join(_PKG, "libmcs.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mcs.h")
 
 MCS_OK, MCS_ERR_INVALID_ARG, MCS_ERR_UNSUPPORTED, MCS_ERR_WORKSPACE, MCS_ERR_HIP = range(5)
+BLOCK_EXACT, BLOCK_MEANPOOL = 0, 1
 
 
 class MCSError(RuntimeError):
@@ -57,6 +61,11 @@ _SIGNATURES = {
     "mcs_residual": (_I, [_DP, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P]),
     "mcs_sparse_attn": (_I, [_DP, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P]),
     "mcs_dense_attn": (_I, [_DP, _P, _P, _P, _F, _P, _P, _P]),
+    "mcs_block_select_workspace_bytes": (_SZ, [_DP, _I, _I, _I]),
+    "mcs_block_select_min_workspace_bytes": (_SZ, [_DP, _I, _I, _I]),
+    "mcs_block_select": (_I, [_DP, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]),
+    "mcs_sparse_attn_counts": (_I, [_DP, _P, _P, _P, _P, _P, _I, _P, _F, _P, _P, _P]),
+    "mcs_residual_counts": (_I, [_DP, _P, _P, _P, _P, _P, _I, _P, _F, _P, _P, _P]),
 }
 
 
@@ -238,3 +247,85 @@ def dense_attn(q, k, v, n_valid: int, group_size: int = 128, scale: Optional[flo
         _stream(stream))
     _check(st, "mcs_dense_attn")
     return o, lse
+
+
+def block_select_workspace_bytes(dims: Dims, mode: int, block: int, nblocks: int,
+                                 minimum: bool = False) -> int:
+    fn = lib().mcs_block_select_min_workspace_bytes if minimum else lib().mcs_block_select_workspace_bytes
+    return int(fn(ctypes.byref(dims), mode, block, nblocks))
+
+
+def block_select(q, k, perm, lse, mode: int, block: int, nblocks: int, n_valid: int,
+                 group_size: int, scale: Optional[float] = None, kv_idx=None, kv_count=None,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """Block selection of the oracle analysis -> (kv_idx [B,H,G,nblocks*block],
+    kv_count [B,H,G]) (mcs_block_select).  `lse` is needed for BLOCK_EXACT and
+    may be None for BLOCK_MEANPOOL."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    G = n_pad // group_size
+    scale = default_scale(d) if scale is None else scale
+    stride = nblocks * block
+    if kv_idx is None:
+        kv_idx = torch.empty((b, h, G, stride), dtype=torch.int32, device=q.device)
+    if kv_count is None:
+        kv_count = torch.empty((b, h, G), dtype=torch.int32, device=q.device)
+    lp = None if lse is None else _need(lse, "lse", torch.float32, (b, h, n_pad))
+    ws = _workspace(block_select_workspace_bytes(dims, mode, block, nblocks), q.device, workspace)
+    st = lib().mcs_block_select(
+        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
+        _need(perm, "perm", torch.int32, (b, h, n_pad)), lp, mode, block, nblocks, scale,
+        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, stride)),
+        _need(kv_count, "kv_count", torch.int32, (b, h, G)),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "mcs_block_select")
+    return kv_idx, kv_count
+
+
+def sparse_attn_counts(q, k, v, perm, kv_idx, kv_count, r, n_valid: int, group_size: int,
+                       scale: Optional[float] = None, o=None, stream=None) -> torch.Tensor:
+    """Reuse step over index rows with per-group counts (mcs_sparse_attn_counts)."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    G = n_pad // group_size
+    stride = kv_idx.shape[-1]
+    scale = default_scale(d) if scale is None else scale
+    if o is None:
+        o = torch.empty_like(q)
+    rp = None if r is None else _need(r, "r", torch.bfloat16, q.shape)
+    st = lib().mcs_sparse_attn_counts(
+        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
+        _need(v, "v", torch.bfloat16, q.shape), _need(perm, "perm", torch.int32, (b, h, n_pad)),
+        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, stride)), stride,
+        _need(kv_count, "kv_count", torch.int32, (b, h, G)), scale, rp,
+        _need(o, "o", torch.bfloat16, q.shape), _stream(stream))
+    _check(st, "mcs_sparse_attn_counts")
+    return o
+
+
+def residual_counts(q, k, v, perm, kv_idx, kv_count, o_full, n_valid: int, group_size: int,
+                    scale: Optional[float] = None, r=None, stream=None) -> torch.Tensor:
+    """R = O_full - SparseAttn over index rows with per-group counts
+    (mcs_residual_counts)."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    G = n_pad // group_size
+    stride = kv_idx.shape[-1]
+    scale = default_scale(d) if scale is None else scale
+    if r is None:
+        r = torch.empty_like(q)
+    st = lib().mcs_residual_counts(
+        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
+        _need(v, "v", torch.bfloat16, q.shape), _need(perm, "perm", torch.int32, (b, h, n_pad)),
+        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, stride)), stride,
+        _need(kv_count, "kv_count", torch.int32, (b, h, G)), scale,
+        _need(o_full, "o_full", torch.bfloat16, q.shape), _need(r, "r", torch.bfloat16, q.shape),
+        _stream(stream))
+    _check(st, "mcs_residual_counts")
+    return r
+
+
+def identity_perm(batch: int, heads: int, n_pad: int, device) -> torch.Tensor:
+    """The partition whose groups are contiguous token blocks (the query blocks
+    of block-sparse attention)."""
+    return torch.arange(n_pad, dtype=torch.int32, device=device).expand(batch, heads, n_pad).contiguous()

@@ -65,10 +65,19 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   for (int kk = 0; kk < KS; ++kk)
     qreg[kk] = *(const bf16x8*)(Qb + (size_t)qrow * D + 16 * kk + 8 * h);
 
-  const int nk = (MODE == ATTN_DENSE) ? p.n_valid : p.topk;
+  // keys of this group: all valid keys (dense), or the first nk indices of
+  // the group's row (a per-group count, clamped to 1 .. row stride, or topk)
+  int nk = p.n_valid;
+  if (MODE != ATTN_DENSE) {
+    nk = p.topk;
+    if (p.kv_count != nullptr) {
+      const int c = p.kv_count[(size_t)bh * G + g];
+      nk = c < 1 ? 1 : (c > p.kv_stride ? p.kv_stride : c);
+    }
+  }
   const int ntiles = (nk + KT - 1) / KT;
   const int32_t* idxrow =
-      (MODE == ATTN_DENSE) ? nullptr : p.kv_idx + ((size_t)bh * G + g) * p.topk;
+      (MODE == ATTN_DENSE) ? nullptr : p.kv_idx + ((size_t)bh * G + g) * p.kv_stride;
 
   // ---- gather geometry ----
   // Copy instruction `ins` (the wavefront's i-th: ins = w*IPW + i) fills
@@ -91,7 +100,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, mat_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, mat_bytes);
   const __amdgpu_buffer_rsrc_t irs =
-      (MODE == ATTN_DENSE) ? krs : make_rsrc(idxrow, (uint32_t)p.topk * 4u);
+      (MODE == ATTN_DENSE) ? krs : make_rsrc(idxrow, (uint32_t)nk * 4u);
   int tok[NTOK];
   auto fetch_idx = [&](int t) {
     const int key0 = t * KT + j4 + r0;

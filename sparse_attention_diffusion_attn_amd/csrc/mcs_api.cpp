@@ -123,6 +123,56 @@ size_t scores_per_head(const mcs_dims* d) {
   return align256((size_t)(d->n_pad / d->group_size) * d->n_valid * sizeof(float));
 }
 
+// ---- block selection ----
+int32_t check_blocks(const mcs_dims* d, int32_t mode, int32_t block, int32_t nblocks) {
+  if (mode != MCS_BLOCK_EXACT && mode != MCS_BLOCK_MEANPOOL)
+    return fail(MCS_ERR_INVALID_ARG, "block selection mode %d unknown", mode);
+  if (block < 1 || block > d->n_valid)
+    return fail(MCS_ERR_INVALID_ARG, "block %d outside 1 .. n_valid (%d)", block, d->n_valid);
+  const int nb = (d->n_valid + block - 1) / block;
+  if (nblocks < 1 || nblocks > nb || nblocks > 1024)
+    return fail(MCS_ERR_INVALID_ARG, "nblocks %d outside 1 .. min(1024, %d blocks)", nblocks, nb);
+  if ((int64_t)nblocks * block > (int64_t)1 << 30)
+    return fail(MCS_ERR_UNSUPPORTED, "nblocks * block too large");
+  return MCS_OK;
+}
+
+struct BlockWs {
+  size_t scores, kbar, bscores, bidx, per_head;
+};
+
+// Per-head workspace of block selection: exact token scores (exact mode) or
+// pooled keys (mean-pool mode), block scores, selected block indices.
+BlockWs block_ws(const mcs_dims* d, int32_t mode, int32_t block, int32_t nblocks) {
+  const size_t G = (size_t)(d->n_pad / d->group_size);
+  const size_t nb = (size_t)((d->n_valid + block - 1) / block);
+  BlockWs w{};
+  size_t o = 0;
+  w.scores = o;
+  if (mode == MCS_BLOCK_EXACT) o = align256(o + G * d->n_valid * sizeof(float));
+  w.kbar = o;
+  if (mode == MCS_BLOCK_MEANPOOL) o = align256(o + nb * d->head_dim * sizeof(double));
+  w.bscores = o; o = align256(o + G * nb * sizeof(float));
+  w.bidx = o;    o = align256(o + G * (size_t)nblocks * sizeof(int32_t));
+  w.per_head = o;
+  return w;
+}
+
+int32_t attn_varlen(int mode, const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                    const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                    int32_t kv_stride, const int32_t* kv_count, float scale, const uint16_t* aux,
+                    uint16_t* out, hipStream_t s) {
+  mcs::AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.kv_count = kv_count;
+  p.aux = aux; p.out = out;
+  p.bh = (int64_t)dims->batch * dims->heads;
+  p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
+  p.groups = dims->n_pad / dims->group_size; p.topk = kv_stride; p.kv_stride = kv_stride;
+  p.scale = scale;
+  return hip_status(mcs::launch_attention(mode, dims->head_dim, dims->group_size, p, s),
+                    mode == mcs::ATTN_SPARSE ? "sparse attention (counts)" : "residual (counts)");
+}
+
 }  // namespace
 
 extern "C" {
@@ -307,7 +357,7 @@ int32_t mcs_residual(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
   p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.aux = o_full; p.out = r;
   p.bh = (int64_t)dims->batch * dims->heads;
   p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
-  p.groups = dims->n_pad / dims->group_size; p.topk = topk; p.scale = scale;
+  p.groups = dims->n_pad / dims->group_size; p.topk = topk; p.kv_stride = topk; p.scale = scale;
   MCS_TRY(hip_status(mcs::launch_attention(mcs::ATTN_RESID, dims->head_dim, dims->group_size, p,
                                            (hipStream_t)stream),
                      "residual"));
@@ -326,10 +376,128 @@ int32_t mcs_sparse_attn(const mcs_dims* dims, const uint16_t* q, const uint16_t*
   p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.aux = r; p.out = o;
   p.bh = (int64_t)dims->batch * dims->heads;
   p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
-  p.groups = dims->n_pad / dims->group_size; p.topk = topk; p.scale = scale;
+  p.groups = dims->n_pad / dims->group_size; p.topk = topk; p.kv_stride = topk; p.scale = scale;
   MCS_TRY(hip_status(mcs::launch_attention(mcs::ATTN_SPARSE, dims->head_dim, dims->group_size, p,
                                            (hipStream_t)stream),
                      "sparse attention"));
+  return ok();
+}
+
+size_t mcs_block_select_workspace_bytes(const mcs_dims* dims, int32_t mode, int32_t block,
+                                        int32_t nblocks) {
+  if (check_dims(dims) != MCS_OK || check_blocks(dims, mode, block, nblocks) != MCS_OK) return 0;
+  return block_ws(dims, mode, block, nblocks).per_head * (size_t)dims->batch * dims->heads;
+}
+
+size_t mcs_block_select_min_workspace_bytes(const mcs_dims* dims, int32_t mode, int32_t block,
+                                            int32_t nblocks) {
+  if (check_dims(dims) != MCS_OK || check_blocks(dims, mode, block, nblocks) != MCS_OK) return 0;
+  return block_ws(dims, mode, block, nblocks).per_head;
+}
+
+int32_t mcs_block_select(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                         const int32_t* perm, const float* lse, int32_t mode, int32_t block,
+                         int32_t nblocks, float scale, int32_t* kv_idx, int32_t* kv_count,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  MCS_TRY(check_dims(dims));
+  MCS_TRY(check_ptr(q, "q"));
+  MCS_TRY(check_ptr(k, "k"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  MCS_TRY(check_blocks(dims, mode, block, nblocks));
+  MCS_TRY(check_ptr(lse, "lse", mode != MCS_BLOCK_EXACT));
+  MCS_TRY(check_ptr(kv_idx, "kv_idx"));
+  MCS_TRY(check_ptr(kv_count, "kv_count"));
+  MCS_TRY(check_scale(scale));
+  const BlockWs w = block_ws(dims, mode, block, nblocks);
+  if (workspace == nullptr || workspace_bytes < w.per_head)
+    return fail(MCS_ERR_WORKSPACE, "workspace needs at least %zu bytes, got %zu", w.per_head,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MCS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t bh = (int64_t)dims->batch * dims->heads;
+  const int G = dims->n_pad / dims->group_size;
+  const int nb = (dims->n_valid + block - 1) / block;
+  const int64_t chunk = std::min<int64_t>(bh, (int64_t)(workspace_bytes / w.per_head));
+  char* ws = (char*)workspace;
+  for (int64_t h0 = 0; h0 < bh; h0 += chunk) {
+    const int64_t hc = std::min<int64_t>(chunk, bh - h0);
+    // per-chunk carve-up: each region sized for hc heads
+    const size_t rs = hc * (w.kbar - w.scores), rk = hc * (w.bscores - w.kbar);
+    const size_t rb = hc * (w.bidx - w.bscores);
+    mcs::BlockParams bp{};
+    bp.q = q; bp.k = k; bp.perm = perm;
+    bp.token_scores = (const float*)ws;
+    bp.kbar = (double*)(ws + rs);
+    bp.block_scores = (float*)(ws + rs + rk);
+    bp.block_idx = (const int32_t*)(ws + rs + rk + rb);
+    bp.kv_idx = kv_idx; bp.kv_count = kv_count;
+    bp.bh0 = h0; bp.bh_count = hc;
+    bp.n_valid = dims->n_valid; bp.n_pad = dims->n_pad; bp.groups = G;
+    bp.block = block; bp.nb = nb; bp.nblocks = nblocks; bp.scale = scale;
+    if (mode == MCS_BLOCK_EXACT) {
+      mcs::ScoreParams sp{};
+      sp.q = q; sp.k = k; sp.perm = perm; sp.lse = lse; sp.scores = (float*)ws;
+      sp.bh0 = h0; sp.bh_count = hc; sp.n_valid = dims->n_valid; sp.n_pad = dims->n_pad;
+      sp.groups = G; sp.scale = scale;
+      MCS_TRY(hip_status(mcs::launch_scores(dims->head_dim, dims->group_size, sp, s), "block scores pass"));
+      MCS_TRY(hip_status(mcs::launch_block_sums(bp, s), "block sums"));
+    } else {
+      MCS_TRY(hip_status(mcs::launch_key_pool(dims->head_dim, bp, s), "key pooling"));
+      MCS_TRY(hip_status(mcs::launch_meanpool_scores(dims->head_dim, dims->group_size, bp, s),
+                         "mean-pooled scores"));
+    }
+    mcs::TopkParams tp{};
+    tp.scores = bp.block_scores; tp.kv_idx = (int32_t*)bp.block_idx; tp.bh0 = 0; tp.bh_count = hc;
+    tp.n_valid = nb; tp.groups = G; tp.topk = nblocks;
+    tp.signed_keys = (mode == MCS_BLOCK_MEANPOOL) ? 1 : 0;
+    MCS_TRY(hip_status(mcs::launch_topk(tp, s), "block top-k"));
+    MCS_TRY(hip_status(mcs::launch_expand_blocks(bp, s), "block expansion"));
+  }
+  return ok();
+}
+
+static int32_t varlen_common(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                             int32_t kv_stride, const int32_t* kv_count, float scale) {
+  MCS_TRY(check_dims(dims));
+  MCS_TRY(check_ptr(q, "q"));
+  MCS_TRY(check_ptr(k, "k"));
+  MCS_TRY(check_ptr(v, "v"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  MCS_TRY(check_ptr(kv_idx, "kv_idx"));
+  MCS_TRY(check_ptr(kv_count, "kv_count"));
+  if (kv_stride < 1)
+    return fail(MCS_ERR_INVALID_ARG, "kv_stride %d must be >= 1", kv_stride);
+  const double idx = (double)dims->batch * dims->heads * (dims->n_pad / dims->group_size) * kv_stride;
+  if (idx >= 9.0e15) return fail(MCS_ERR_UNSUPPORTED, "kv_idx too large");
+  MCS_TRY(check_scale(scale));
+  return MCS_OK;
+}
+
+int32_t mcs_sparse_attn_counts(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                               int32_t kv_stride, const int32_t* kv_count, float scale,
+                               const uint16_t* r, uint16_t* o, void* stream) {
+  MCS_TRY(varlen_common(dims, q, k, v, perm, kv_idx, kv_stride, kv_count, scale));
+  MCS_TRY(check_ptr(r, "r", true));
+  MCS_TRY(check_ptr(o, "o"));
+  if (o == q || o == k || o == v || (r != nullptr && o == r))
+    return fail(MCS_ERR_INVALID_ARG, "o must not alias q, k, v or r");
+  MCS_TRY(attn_varlen(mcs::ATTN_SPARSE, dims, q, k, v, perm, kv_idx, kv_stride, kv_count, scale, r,
+                      o, (hipStream_t)stream));
+  return ok();
+}
+
+int32_t mcs_residual_counts(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
+                            int32_t kv_stride, const int32_t* kv_count, float scale,
+                            const uint16_t* o_full, uint16_t* r, void* stream) {
+  MCS_TRY(varlen_common(dims, q, k, v, perm, kv_idx, kv_stride, kv_count, scale));
+  MCS_TRY(check_ptr(o_full, "o_full"));
+  MCS_TRY(check_ptr(r, "r"));
+  MCS_TRY(attn_varlen(mcs::ATTN_RESID, dims, q, k, v, perm, kv_idx, kv_stride, kv_count, scale,
+                      o_full, r, (hipStream_t)stream));
   return ok();
 }
 

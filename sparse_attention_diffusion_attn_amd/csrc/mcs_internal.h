@@ -14,12 +14,14 @@ struct AttnParams {
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* perm;    // sparse / resid: query rows of each group
-  const int32_t* kv_idx;  // sparse / resid: [BH, G, topk]
+  const int32_t* kv_idx;  // sparse / resid: [BH, G, kv_stride]
+  const int32_t* kv_count;  // sparse / resid: [BH, G] keys per group, or NULL (= topk)
   const uint16_t* aux;    // sparse: residual to add (nullable); resid: O_full
   uint16_t* out;          // O (dense, sparse) or R (resid)
   float* lse;             // dense: nullable
   int64_t bh;             // batch * heads
   int32_t n_valid, n_pad, groups, topk;
+  int32_t kv_stride;      // row stride of kv_idx (>= every count)
   float scale;
 };
 
@@ -39,6 +41,24 @@ struct TopkParams {
   int32_t* kv_idx;        // [BH, G, topk], written for heads bh0 ..
   int64_t bh0, bh_count;
   int32_t n_valid, groups, topk;
+  int32_t signed_keys;    // 0: scores >= 0; 1: any finite scores
+};
+
+// Block selection (variants of the oracle analysis): KV blocks of `block`
+// consecutive valid keys, the last one possibly shorter.
+struct BlockParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const int32_t* perm;
+  const float* token_scores;  // exact mode: [bh_count, G, n_valid]
+  double* kbar;               // mean-pool mode: [bh_count, NB, d]
+  float* block_scores;        // [bh_count, G, NB]
+  const int32_t* block_idx;   // expansion: [bh_count, G, nblocks], ascending
+  int32_t* kv_idx;            // expansion: [BH, G, nblocks*block] tokens
+  int32_t* kv_count;          // expansion: [BH, G]
+  int64_t bh0, bh_count;
+  int32_t n_valid, n_pad, groups, block, nb, nblocks;
+  float scale;
 };
 
 struct PddpParams {
@@ -58,6 +78,10 @@ hipError_t launch_attention(int mode, int head_dim, int group_size, const AttnPa
                             hipStream_t s);
 hipError_t launch_scores(int head_dim, int group_size, const ScoreParams& p, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+hipError_t launch_block_sums(const BlockParams& p, hipStream_t s);
+hipError_t launch_key_pool(int head_dim, const BlockParams& p, hipStream_t s);
+hipError_t launch_meanpool_scores(int head_dim, int group_size, const BlockParams& p, hipStream_t s);
+hipError_t launch_expand_blocks(const BlockParams& p, hipStream_t s);
 
 hipError_t launch_pddp_identity(const PddpParams& p, hipStream_t s);
 // stage: 0 = node means, 1 = one power-iteration step, 2 = projections

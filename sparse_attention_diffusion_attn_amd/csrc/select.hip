@@ -190,6 +190,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   const int g = work - (int)(bl * G);
   const int n = p.n_valid;
   const uint32_t* a = (const uint32_t*)(p.scores + ((size_t)bl * G + g) * (size_t)n);
+  // order-preserving unsigned key of a score (the bit pattern itself for
+  // non-negative scores; sign-folded, with -0 = +0, for signed ones)
+  const bool sgn = p.signed_keys != 0;
+  auto key = [sgn](uint32_t u) -> uint32_t {
+    if (!sgn) return u;
+    if (u == 0x80000000u) u = 0u;
+    return (u >> 31) ? ~u : (u | 0x80000000u);
+  };
   int32_t* out = p.kv_idx + ((size_t)(p.bh0 + bl) * G + g) * (size_t)p.topk;
   const int tid = threadIdx.x;
 
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     for (int b = tid; b < NBIN; b += NT) hist[b] = 0;
     __syncthreads();
     for (int j = tid; j < n; j += NT) {
-      const uint32_t u = a[j];
+      const uint32_t u = key(a[j]);
       if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & dmask], 1);
     }
     __syncthreads();
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = base + tid * E + e;
-      u[e] = (j < n) ? a[j] : 0u;
+      u[e] = (j < n) ? key(a[j]) : 0u;
       if (j < n && u[e] == T) ++neq;
     }
     int eq_tot;

@@ -22,6 +22,9 @@ MAX_ABS = 2e-2
 MEAN_ABS = 1e-3
 EPS_SEL = 1e-6
 EPS_PDDP = 1e-9
+# block selections (oracle-analysis variants): block scores are fp64 sums
+# ranked in fp32 on the GPU; ties are resolved within EPS_BLK * max|score|
+EPS_BLK = 1e-5
 
 
 def bf16_to_f64(t) -> np.ndarray:
@@ -56,6 +59,28 @@ def check_selection(gpu_idx, a_row, k):
     must = np.nonzero(a_row > tau + EPS_SEL)[0]
     assert np.all(np.isin(must, gpu_idx)), "a clearly selected key is missing"
     assert np.all(a_row[gpu_idx] >= tau_next - EPS_SEL), "a clearly rejected key was selected"
+    return "band"
+
+
+def check_block_selection(gpu_blocks, scores_row, n_b):
+    """Compare one group's GPU block set with the oracle's block scores: equal
+    outside a relative tie band, else every clearly better block present and no
+    clearly worse one.  Returns 'strict' or 'band'."""
+    gpu_blocks = np.asarray(gpu_blocks)
+    scores_row = np.asarray(scores_row, np.float64)
+    assert len(gpu_blocks) == n_b
+    assert np.all(np.diff(gpu_blocks) > 0), "blocks not strictly ascending"
+    eps = EPS_BLK * max(1e-30, float(np.abs(scores_row).max()))
+    ref = orc.topk_select(scores_row[None], n_b)[0]
+    srt = np.sort(scores_row)[::-1]
+    tau = srt[n_b - 1]
+    tau_next = srt[n_b] if n_b < len(scores_row) else -np.inf
+    if tau - tau_next >= eps:
+        assert np.array_equal(gpu_blocks, ref), "block selection differs outside the tie band"
+        return "strict"
+    must = np.nonzero(scores_row > tau + eps)[0]
+    assert np.all(np.isin(must, gpu_blocks)), "a clearly selected block is missing"
+    assert np.all(scores_row[gpu_blocks] >= tau_next - eps), "a clearly rejected block was selected"
     return "band"
 
 

@@ -119,3 +119,38 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         mcs.dense_attn(q, q, q, 128, 64)
+
+
+def test_block_select_checks():
+    lib = mcs.lib()
+    dm = d()                       # n_valid 1000, C 128, 2 heads
+    b = ctypes.byref(dm)
+    ws = lib.mcs_block_select_workspace_bytes(b, mcs.BLOCK_EXACT, 64, 4)
+    mn = lib.mcs_block_select_min_workspace_bytes(b, mcs.BLOCK_EXACT, 64, 4)
+    G, NB = 8, 16
+    per_head = sum((x + 255) // 256 * 256 for x in (G * 1000 * 4, G * NB * 4, G * 4 * 4))
+    assert mn == per_head and ws == 2 * per_head
+    per_head_mp = sum((x + 255) // 256 * 256 for x in (NB * 128 * 8, G * NB * 4, G * 4 * 4))
+    assert lib.mcs_block_select_min_workspace_bytes(b, mcs.BLOCK_MEANPOOL, 64, 4) == per_head_mp
+    assert lib.mcs_block_select_workspace_bytes(b, 7, 64, 4) == 0
+    call = lambda mode, blk, nb, lse=P, wsb=1 << 30: lib.mcs_block_select(  # noqa: E731
+        b, P, P, P, lse, mode, blk, nb, 0.1, P, P, P, wsb, None)
+    assert call(2, 64, 4) == mcs.MCS_ERR_INVALID_ARG and "mode" in err()
+    assert call(mcs.BLOCK_EXACT, 0, 4) == mcs.MCS_ERR_INVALID_ARG and "block" in err()
+    assert call(mcs.BLOCK_EXACT, 64, 17) == mcs.MCS_ERR_INVALID_ARG and "nblocks" in err()
+    assert call(mcs.BLOCK_EXACT, 1, 1001) == mcs.MCS_ERR_INVALID_ARG and "nblocks" in err()
+    assert call(mcs.BLOCK_EXACT, 64, 4, lse=None) == mcs.MCS_ERR_INVALID_ARG and "lse" in err()
+    assert call(mcs.BLOCK_EXACT, 64, 4, wsb=mn - 1) == mcs.MCS_ERR_WORKSPACE
+
+
+def test_counts_calls_checks():
+    lib = mcs.lib()
+    b = ctypes.byref(d())
+    assert lib.mcs_sparse_attn_counts(b, P, P, P, P, P, 0, P, 0.1, None, P + 256, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "kv_stride" in err()
+    assert lib.mcs_sparse_attn_counts(b, P, P, P, P, P, 8, None, 0.1, None, P + 256, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "kv_count" in err()
+    assert lib.mcs_residual_counts(b, P, P, P, P, P, 8, P, 0.1, None, P + 256, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "o_full" in err()
+    assert lib.mcs_sparse_attn_counts(b, P, P, P, P, P, 8, P, 0.1, None, P, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "alias" in err()
