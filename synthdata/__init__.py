@@ -15,6 +15,18 @@ Each reuse step adds drift * N(0, 1) to the fp32 masters of Q, K and V (per
 head, Q then K then V) and re-quantises.  fp32 -> bf16 is round-to-nearest-even.
 Rows N .. N_pad-1 (padding up to a multiple of the query tile C) are zero.
 
+Label layouts:
+  "random" (default)  the uniform draw above: a cluster's tokens are scattered
+                      over the whole sequence, so contiguous token blocks mix
+                      many clusters (the adversarial case for block layouts).
+  "grid"              the same draws are made (so every other value is
+                      unchanged), then each token of the latent grid
+                      (frames x rows x cols, row-major, the layer's `grid`)
+                      takes the label of its spatial cell: the rows x cols
+                      plane is cut into cy x cx cells, cy*cx = n_clusters, the
+                      same cells in every frame (objects persist over time),
+                      so contiguous token blocks see one or two clusters.
+
 The cluster structure stands in for the observation on the MC-Sparse pages that
 attention mass concentrates on a small number of token interactions (onedev.kr
 summary, section "what it is"); no model weights or dataset items are used.
@@ -42,6 +54,8 @@ class LayerConfig:
     drift: float
     power_iters: int = 20
     seed: int = 0
+    grid: tuple = ()          # (frames, rows, cols) of the latent, frames*rows*cols = N
+    layout: str = "random"    # "random" or "grid" (see the module docstring)
 
     @property
     def n_pad(self) -> int:
@@ -70,12 +84,14 @@ class LayerConfig:
 
 
 CONFIGS = {
-    "tiny": LayerConfig("tiny", 1, 1, 1024, 64, 64, 25, 16, 0.3, 1, 0.05),
-    "480p": LayerConfig("480p", 1, 24, 32760, 128, 128, 25, 64, 0.3, 4, 0.05),
-    "wan720p": LayerConfig("wan720p", 1, 40, 75600, 128, 128, 15, 64, 0.3, 8, 0.05),
-    "hunyuan720p_15": LayerConfig("hunyuan720p_15", 1, 24, 118800, 128, 128, 15, 128, 0.3, 8, 0.05),
-    "hunyuan720p_25": LayerConfig("hunyuan720p_25", 1, 24, 118800, 128, 128, 25, 128, 0.3, 8, 0.05),
-    "3d": LayerConfig("3d", 1, 16, 65536, 64, 128, 15, 256, 0.2, 10, 0.03),
+    "tiny": LayerConfig("tiny", 1, 1, 1024, 64, 64, 25, 16, 0.3, 1, 0.05, grid=(1, 32, 32)),
+    "480p": LayerConfig("480p", 1, 24, 32760, 128, 128, 25, 64, 0.3, 4, 0.05, grid=(13, 42, 60)),
+    "wan720p": LayerConfig("wan720p", 1, 40, 75600, 128, 128, 15, 64, 0.3, 8, 0.05, grid=(21, 45, 80)),
+    "hunyuan720p_15": LayerConfig("hunyuan720p_15", 1, 24, 118800, 128, 128, 15, 128, 0.3, 8, 0.05,
+                                  grid=(33, 45, 80)),
+    "hunyuan720p_25": LayerConfig("hunyuan720p_25", 1, 24, 118800, 128, 128, 25, 128, 0.3, 8, 0.05,
+                                  grid=(33, 45, 80)),
+    "3d": LayerConfig("3d", 1, 16, 65536, 64, 128, 15, 256, 0.2, 10, 0.03, grid=(1, 256, 256)),
 }
 
 
@@ -83,6 +99,19 @@ def custom(name="custom", batch=1, heads=1, n_valid=512, head_dim=64, group_size
            density_pct=25, n_clusters=8, sigma=0.3, n_reuse=1, drift=0.05, seed=0) -> LayerConfig:
     return LayerConfig(name, batch, heads, n_valid, head_dim, group_size, density_pct,
                        n_clusters, sigma, n_reuse, drift, seed=seed)
+
+
+def grid_labels(cfg: LayerConfig) -> torch.Tensor:
+    """Cluster label of every token under the "grid" layout (int64 [N])."""
+    f, rows, cols = cfg.grid
+    assert f * rows * cols == cfg.n_valid, "grid does not cover the tokens"
+    n = cfg.n_clusters
+    cy = max(c for c in range(1, int(n ** 0.5) + 1) if n % c == 0)
+    cx = n // cy
+    y = torch.arange(rows).repeat_interleave(cols)
+    x = torch.arange(cols).repeat(rows)
+    cell = (y * cy // rows) * cx + (x * cx // cols)
+    return cell.repeat(f)
 
 
 def _to_bf16_padded(x: torch.Tensor, n_pad: int) -> torch.Tensor:
@@ -111,6 +140,8 @@ def generate(cfg: LayerConfig, steps: int | None = None, heads: List[int] | None
         for h in range(H):
             centres = torch.randn((cfg.n_clusters, d), generator=g)
             labels = torch.randint(0, cfg.n_clusters, (N,), generator=g)
+            if cfg.layout == "grid":
+                labels = grid_labels(cfg)
             q = centres[labels] + cfg.sigma * torch.randn((N, d), generator=g)
             k = centres[labels] + cfg.sigma * torch.randn((N, d), generator=g)
             v = torch.randn((N, d), generator=g)
