@@ -28,7 +28,10 @@ mcs_residual, mcs_sparse_attn, mcs_dense_attn); this module only orders calls,
 copies and events.  Both streams have the default priority.
 
 Usage: python -m sparse_attention_diffusion_attn_amd.driver [--config 480p]
-       [--layers 8] [--steps 6]
+       [--layers 8] [--steps 6]                      offload vs resident
+       python -m sparse_attention_diffusion_attn_amd.driver --schedule
+       [--config 480p] [--n-steps 50] [--warmup 10] [--refresh 0,20,10]
+                                                     a whole denoising run
 """
 from __future__ import annotations
 
@@ -223,16 +226,66 @@ class Stack:
             self.step(step, kind, None if outs_per_step is None else outs_per_step[step])
 
 
+def schedule_run(cfg, n_steps: int, warmup: int, refreshes, dev="cuda:0"):
+    """One layer over whole denoising schedules: per-kind step times, the
+    effective density (attention time / that of all-dense steps) and the
+    anchor overhead spread over the run (R23 over a schedule)."""
+    import synthdata as sd
+    shape = LayerShape(cfg.batch, cfg.heads, cfg.n_valid, cfg.n_pad, cfg.head_dim, cfg.group_size, cfg.topk)
+    (q0, k0, v0), (q1, k1, v1) = [tuple(t.to(dev) for t in s) for s in sd.generate(cfg, steps=2)]
+    inputs = lambda layer, step: (q0, k0, v0) if step % 2 == 0 else (q1, k1, v1)  # noqa: E731
+    stack = Stack(1, shape, inputs, False, cfg.scale, cfg.power_iters, dev)
+    o = [torch.empty_like(q0)]
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(kind, reps):
+        ts = []
+        for r in range(reps + 1):
+            a, b = ev(), ev()
+            a.record()
+            stack.step(r, kind, o)
+            b.record()
+            torch.cuda.synchronize()
+            if r:
+                ts.append(a.elapsed_time(b))
+        return sum(ts) / len(ts)
+
+    t = {"dense": timed("dense", 3), "anchor": timed("anchor", 2), "reuse": timed("reuse", 5)}
+    rows = []
+    for r in refreshes:
+        kinds = Schedule(n_steps, warmup, r).kinds()
+        total = sum(t[k] for k in kinds)
+        n_anchor = kinds.count("anchor")
+        rows.append({
+            "n_steps": n_steps, "warmup": warmup, "refresh": r, "anchors": n_anchor,
+            "dense_steps": kinds.count("dense"), "reuse_steps": kinds.count("reuse"),
+            "ms_total": round(total, 2), "ms_all_dense": round(n_steps * t["dense"], 2),
+            "speedup_vs_dense": round(n_steps * t["dense"] / total, 3),
+            # anchors beyond the dense step they replace, in dense-step units per step
+            "delta_s": round(n_anchor * (t["anchor"] - t["dense"]) / t["dense"] / n_steps, 4),
+        })
+    return {k: round(v, 3) for k, v in t.items()}, rows
+
+
 def main():
     import synthdata as sd
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="480p")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--steps", type=int, default=6, help="reuse steps timed after one anchor")
+    ap.add_argument("--schedule", action="store_true", help="time whole denoising schedules")
+    ap.add_argument("--n-steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--refresh", default="0,20,10")
     args = ap.parse_args()
     assert torch.cuda.is_available(), "the driver runs on the GPU"
     mcs.lib()
     cfg = sd.CONFIGS[args.config]
+    if args.schedule:
+        t, rows = schedule_run(cfg, args.n_steps, args.warmup, [int(x) for x in args.refresh.split(",")])
+        print(json.dumps({"workload": f"{args.config} attention layer, whole schedules",
+                          "density_pct": cfg.density_pct, "ms_per_step": t, "schedules": rows}))
+        return
     dev = "cuda:0"
     shape = LayerShape(cfg.batch, cfg.heads, cfg.n_valid, cfg.n_pad, cfg.head_dim, cfg.group_size, cfg.topk)
     (q0, k0, v0), (q1, k1, v1) = [tuple(t.to(dev) for t in s) for s in sd.generate(cfg, steps=2)]
