@@ -119,8 +119,13 @@ GroupWs group_ws(const mcs_dims* d) {
   return w;
 }
 
-size_t scores_per_head(const mcs_dims* d) {
+// per head: the group scores [G, n_valid] fp32, then the top-10-bit histogram
+// of each group's row [G, 1024] int32 written by the score pass
+size_t scores_bytes(const mcs_dims* d) {
   return align256((size_t)(d->n_pad / d->group_size) * d->n_valid * sizeof(float));
+}
+size_t scores_per_head(const mcs_dims* d) {
+  return scores_bytes(d) + align256((size_t)(d->n_pad / d->group_size) * 1024 * sizeof(int32_t));
 }
 
 // ---- block selection ----
@@ -320,14 +325,17 @@ int32_t mcs_anchor_select(const mcs_dims* dims, const uint16_t* q, const uint16_
   const int64_t chunk = std::min<int64_t>(bh, (int64_t)(workspace_bytes / per_head));
   for (int64_t h0 = 0; h0 < bh; h0 += chunk) {
     const int64_t hc = std::min<int64_t>(chunk, bh - h0);
+    // scores of hc heads, then their histograms
+    int32_t* hist = (int32_t*)((char*)workspace + hc * scores_bytes(dims));
     mcs::ScoreParams sp{};
     sp.q = q; sp.k = k; sp.perm = perm; sp.lse = lse; sp.scores = (float*)workspace;
+    sp.hist = hist;
     sp.bh0 = h0; sp.bh_count = hc; sp.n_valid = dims->n_valid; sp.n_pad = dims->n_pad;
     sp.groups = G; sp.scale = scale;
     MCS_TRY(hip_status(mcs::launch_scores(dims->head_dim, dims->group_size, sp, s), "anchor pass 2"));
     mcs::TopkParams tp{};
     tp.scores = (const float*)workspace; tp.kv_idx = kv_idx; tp.bh0 = h0; tp.bh_count = hc;
-    tp.n_valid = dims->n_valid; tp.groups = G; tp.topk = topk;
+    tp.n_valid = dims->n_valid; tp.groups = G; tp.topk = topk; tp.hist0 = hist;
     MCS_TRY(hip_status(mcs::launch_topk(tp, s), "top-k"));
   }
   return ok();

@@ -31,6 +31,7 @@ struct ScoreParams {
   const int32_t* perm;
   const float* lse;
   float* scores;          // [bh_count, G, n_valid]
+  int32_t* hist;          // [bh_count, G, 1024] top-10-bit histogram of each row, or NULL
   int64_t bh0, bh_count;  // heads [bh0, bh0 + bh_count)
   int32_t n_valid, n_pad, groups;
   float scale;
@@ -42,6 +43,8 @@ struct TopkParams {
   int64_t bh0, bh_count;
   int32_t n_valid, groups, topk;
   int32_t signed_keys;    // 0: scores >= 0; 1: any finite scores
+  const int32_t* hist0;   // [bh_count, G, 1024] histogram of the top 10 key bits
+                          // from the score pass (unsigned keys), or NULL
 };
 
 // Block selection (variants of the oracle analysis): KV blocks of `block`

@@ -11,7 +11,7 @@
 // lane exchange and a fixed-order add of the wavefronts' partials in LDS.
 //
 // topk_kernel: one workgroup per (head, group).  Exact radix select on the
-// fp32 bit patterns of the non-negative scores (11/11/10-bit digits, LDS
+// fp32 bit patterns of the non-negative scores (10/11/11-bit digits, LDS
 // histograms with integer atomics), then an order-preserving compaction that
 // keeps every key above the threshold and the lowest-index keys equal to it,
 // written in ascending key order.  Integer counts only, so it is exact and
@@ -33,6 +33,7 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
 
   __shared__ __attribute__((aligned(1024))) char lds[2 * TILE];
   __shared__ float red[2][NW][KT];
+  __shared__ int hist_s[1024];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -93,13 +94,22 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
   // Column sums of tile t are finished (fixed wavefront order) by the first
   // KT threads after the barrier at the top of tile t+1; the partials are
   // double-buffered so one barrier per tile suffices.
+  // With p.hist, the top 10 bits of every score (its fp32 pattern; scores are
+  // >= 0) are also counted, so the top-k pass can skip its first scan.
+  const bool want_hist = p.hist != nullptr;
+  if (want_hist) {
+    for (int b = threadIdx.x; b < 1024; b += blockDim.x) hist_s[b] = 0;
+  }
   auto finish = [&](int t) {
     if (threadIdx.x < KT) {
       const int key = t * KT + threadIdx.x;
       float a = red[t & 1][0][threadIdx.x];
 #pragma unroll
       for (int ww = 1; ww < NW; ++ww) a += red[t & 1][ww][threadIdx.x];
-      if (key < nk) out[key] = a;
+      if (key < nk) {
+        out[key] = a;
+        if (want_hist) atomicAdd(&hist_s[__float_as_uint(a) >> 22], 1);
+      }
     }
   };
 
@@ -149,6 +159,11 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
   }
   __syncthreads();
   finish(ntiles - 1);
+  if (want_hist) {
+    __syncthreads();
+    int32_t* hg = p.hist + ((size_t)bl * G + g) * 1024;
+    for (int b = threadIdx.x; b < 1024; b += blockDim.x) hg[b] = hist_s[b];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -203,17 +218,23 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
 
   uint32_t prefix = 0u, pmask = 0u;
   int krem = p.topk;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
+  const int shifts[3] = {22, 11, 0};
+  const int widths[3] = {10, 11, 11};
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int sh = shifts[pass];
     const uint32_t dmask = (1u << widths[pass]) - 1u;
-    for (int b = tid; b < NBIN; b += NT) hist[b] = 0;
-    __syncthreads();
-    for (int j = tid; j < n; j += NT) {
-      const uint32_t u = key(a[j]);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & dmask], 1);
+    if (pass == 0 && p.hist0 != nullptr) {
+      // the score pass already counted the top 10 bits of this row
+      const int32_t* h0 = p.hist0 + ((size_t)bl * G + g) * 1024;
+      for (int b = tid; b < NBIN; b += NT) hist[b] = (b < 1024) ? h0[b] : 0;
+    } else {
+      for (int b = tid; b < NBIN; b += NT) hist[b] = 0;
+      __syncthreads();
+      for (int j = tid; j < n; j += NT) {
+        const uint32_t u = key(a[j]);
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & dmask], 1);
+      }
     }
     __syncthreads();
     // thread t owns bins, highest first: NBIN-1-BPT*t-i for i = 0..BPT-1

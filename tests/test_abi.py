@@ -41,7 +41,7 @@ def test_workspace_sizes():
     for nbytes in (bh * G * D * 8,) * 3 + (bh * 1024 * 8, bh * 1024 * 4):
         want = (want + nbytes + 255) // 256 * 256
     assert lib.mcs_group_workspace_bytes(ctypes.byref(dm)) == want
-    per_head = (G * 1000 * 4 + 255) // 256 * 256
+    per_head = (G * 1000 * 4 + 255) // 256 * 256 + (G * 1024 * 4 + 255) // 256 * 256
     assert lib.mcs_anchor_select_min_workspace_bytes(ctypes.byref(dm), 250) == per_head
     assert lib.mcs_anchor_select_workspace_bytes(ctypes.byref(dm), 250) == 2 * per_head
     assert lib.mcs_anchor_select_workspace_bytes(ctypes.byref(dm), 0) == 0
