@@ -24,8 +24,10 @@
  *
  * Conventions shared by every call
  * --------------------------------
- * Tensors are device pointers to contiguous row-major arrays.  bf16 values are
- * passed as uint16_t bit patterns.  Shapes use the dims struct:
+ * Tensors are device pointers to contiguous row-major arrays (Q, K, V and the
+ * layer output may also be strided views: see the `_strided` calls at the
+ * end).  bf16 values are passed as uint16_t bit patterns.  Shapes use the dims
+ * struct:
  *   Q, K, V, O, O_full, R : bf16  [batch, heads, n_pad, head_dim]
  *   lse                   : fp32  [batch, heads, n_pad]   (natural log)
  *   perm                  : int32 [batch, heads, n_pad]   group g = perm[g*C .. g*C+C-1]
@@ -66,7 +68,7 @@
 extern "C" {
 #endif
 
-#define MCS_ABI_VERSION 1
+#define MCS_ABI_VERSION 2
 
 typedef enum {
   MCS_OK = 0,
@@ -220,6 +222,69 @@ int32_t mcs_residual_counts(const mcs_dims* dims, const uint16_t* q, const uint1
                             const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
                             int32_t kv_stride, const int32_t* kv_count, float scale,
                             const uint16_t* o_full, uint16_t* r, void* stream);
+
+/*
+ * Strided inputs and outputs.  A DiT block usually produces Q, K and V as
+ * [batch, tokens, heads, head_dim] (BNHD), often as slices of one fused QKV
+ * projection, and consumes the attention output in that layout too.  The
+ * `_strided` calls below are the calls above with Q, K, V and the layer output
+ * given as strided views instead of contiguous [B,H,n_pad,d] arrays; results
+ * are bitwise the same as for contiguous copies of the same values.
+ *
+ * mcs_strides: element strides of a bf16 tensor seen as [B, H, n_pad, d] whose
+ * rows (d values) are contiguous: row (b, h, n) starts at element
+ * b*batch + h*head + n*token of the pointer passed.  The stride of a dimension
+ * of extent 1 is ignored.  Every other stride must be a multiple of 8 elements
+ * (16-byte rows), 0 <= stride < 2^40, token < 2^23, one head's rows must span
+ * less than 4 GiB ((n_pad-1)*token*2 + 2d bytes) and the whole view less than
+ * 2^40 elements.  The tensors still hold n_pad rows per head, the padding rows
+ * zero-filled in Q, K and V as above.
+ *
+ * mcs_layout: strides of q, k, v and of o, the layer output: O of
+ * mcs_sparse_attn_strided and mcs_dense_attn_strided, O_full of
+ * mcs_anchor_select_strided (and read back by mcs_residual_strided).  k and v
+ * must share the token stride (MCS_ERR_UNSUPPORTED otherwise); the rows of o
+ * must not overlap (MCS_ERR_INVALID_ARG).  lse, perm, kv_idx and R stay
+ * contiguous as above.  A NULL layout means all contiguous, i.e. the
+ * unstrided calls.
+ */
+typedef struct {
+  int64_t batch;
+  int64_t head;
+  int64_t token;
+} mcs_strides;
+
+typedef struct {
+  mcs_strides q;
+  mcs_strides k;
+  mcs_strides v;
+  mcs_strides o;
+} mcs_layout;
+
+/* Fill `layout` for contiguous [B,H,n_pad,d] tensors (the unstrided calls). */
+void mcs_layout_bhnd(const mcs_dims* dims, mcs_layout* layout);
+/* Fill `layout` for four separate contiguous [B,n_pad,H,d] tensors. */
+void mcs_layout_bnhd(const mcs_dims* dims, mcs_layout* layout);
+
+int32_t mcs_group_strided(const mcs_dims* dims, const mcs_layout* layout, const uint16_t* q,
+                          int32_t power_iters, int32_t max_levels, int32_t* perm,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int32_t mcs_anchor_select_strided(const mcs_dims* dims, const mcs_layout* layout,
+                                  const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const int32_t* perm, int32_t topk, float scale,
+                                  uint16_t* o_full, float* lse, int32_t* kv_idx,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+int32_t mcs_residual_strided(const mcs_dims* dims, const mcs_layout* layout, const uint16_t* q,
+                             const uint16_t* k, const uint16_t* v, const int32_t* perm,
+                             const int32_t* kv_idx, int32_t topk, float scale,
+                             const uint16_t* o_full, uint16_t* r, void* stream);
+int32_t mcs_sparse_attn_strided(const mcs_dims* dims, const mcs_layout* layout,
+                                const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* perm, const int32_t* kv_idx, int32_t topk,
+                                float scale, const uint16_t* r, uint16_t* o, void* stream);
+int32_t mcs_dense_attn_strided(const mcs_dims* dims, const mcs_layout* layout,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               float scale, uint16_t* o, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -42,12 +42,21 @@ class Dims(ctypes.Structure):
                 ("n_pad", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32)]
 
 
+class Strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("q", Strides), ("k", Strides), ("v", Strides), ("o", Strides)]
+
+
 _LIB: Optional[ctypes.CDLL] = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _SZ = ctypes.c_size_t
 _F = ctypes.c_float
 _DP = ctypes.POINTER(Dims)
+_LP = ctypes.POINTER(Layout)
 
 _SIGNATURES = {
     "mcs_abi_version": (_I, []),
@@ -66,6 +75,13 @@ _SIGNATURES = {
     "mcs_block_select": (_I, [_DP, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]),
     "mcs_sparse_attn_counts": (_I, [_DP, _P, _P, _P, _P, _P, _I, _P, _F, _P, _P, _P]),
     "mcs_residual_counts": (_I, [_DP, _P, _P, _P, _P, _P, _I, _P, _F, _P, _P, _P]),
+    "mcs_layout_bhnd": (None, [_DP, _LP]),
+    "mcs_layout_bnhd": (None, [_DP, _LP]),
+    "mcs_group_strided": (_I, [_DP, _LP, _P, _I, _I, _P, _P, _SZ, _P]),
+    "mcs_anchor_select_strided": (_I, [_DP, _LP, _P, _P, _P, _P, _I, _F, _P, _P, _P, _P, _SZ, _P]),
+    "mcs_residual_strided": (_I, [_DP, _LP, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P]),
+    "mcs_sparse_attn_strided": (_I, [_DP, _LP, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P]),
+    "mcs_dense_attn_strided": (_I, [_DP, _LP, _P, _P, _P, _F, _P, _P, _P]),
 }
 
 
@@ -128,6 +144,33 @@ def _need(t: torch.Tensor, name: str, dtype, shape) -> int:
     return t.data_ptr()
 
 
+def _view(t: torch.Tensor, name: str, shape) -> int:
+    """A bf16 device tensor of `shape` [B, H, n_pad, d] whose rows are
+    contiguous (stride 1 along d); other strides are passed in a Layout."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be torch.bfloat16, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have contiguous rows (stride 1 along head_dim)")
+    return t.data_ptr()
+
+
+def _strides(t: torch.Tensor) -> Strides:
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def layout_of(q, k, v, o) -> Optional[Layout]:
+    """None if q, k, v and o are all contiguous, else their Layout."""
+    if all(t.is_contiguous() for t in (q, k, v, o)):
+        return None
+    return Layout(_strides(q), _strides(k), _strides(v), _strides(o))
+
+
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
 
@@ -150,23 +193,37 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
 def group(q: torch.Tensor, n_valid: int, group_size: int, power_iters: int = 20,
           max_levels: int = -1, perm: Optional[torch.Tensor] = None,
           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Fast PDDP grouping -> perm int32 [B, H, n_pad] (mcs_group)."""
+    """Fast PDDP grouping -> perm int32 [B, H, n_pad] (mcs_group).  `q` may be
+    a strided [B, H, n_pad, d] view with contiguous rows (mcs_group_strided)."""
     dims = _dims_of(q, n_valid, group_size)
     b, h, n_pad, d = q.shape
     if perm is None:
         perm = torch.empty((b, h, n_pad), dtype=torch.int32, device=q.device)
     ws = _workspace(group_workspace_bytes(dims), q.device, workspace)
-    st = lib().mcs_group(ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), power_iters,
-                         max_levels, _need(perm, "perm", torch.int32, (b, h, n_pad)),
-                         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    qp = _view(q, "q", q.shape)
+    pp = _need(perm, "perm", torch.int32, (b, h, n_pad))
+    wsp, wsn = ws.data_ptr(), ws.numel() * ws.element_size()
+    if q.is_contiguous():
+        st = lib().mcs_group(ctypes.byref(dims), qp, power_iters, max_levels, pp, wsp, wsn,
+                             _stream(stream))
+    else:
+        lay = Layout(_strides(q), _strides(q), _strides(q), _strides(q))
+        st = lib().mcs_group_strided(ctypes.byref(dims), ctypes.byref(lay), qp, power_iters,
+                                     max_levels, pp, wsp, wsn, _stream(stream))
     _check(st, "mcs_group")
     return perm
+
+
+def _contig_out(q: torch.Tensor) -> torch.Tensor:
+    return torch.empty(q.shape, dtype=q.dtype, device=q.device)
 
 
 def anchor_select(q, k, v, perm, n_valid: int, group_size: int, topk: int,
                   scale: Optional[float] = None, o_full=None, lse=None, kv_idx=None,
                   workspace: Optional[torch.Tensor] = None, stream=None):
-    """Two-pass exact selection -> (o_full, lse, kv_idx) (mcs_anchor_select)."""
+    """Two-pass exact selection -> (o_full, lse, kv_idx) (mcs_anchor_select).
+    q, k, v and o_full may be strided views (mcs_anchor_select_strided); the
+    default o_full has q's layout where torch can reproduce it."""
     dims = _dims_of(q, n_valid, group_size)
     b, h, n_pad, d = q.shape
     G = n_pad // group_size
@@ -178,33 +235,41 @@ def anchor_select(q, k, v, perm, n_valid: int, group_size: int, topk: int,
     if kv_idx is None:
         kv_idx = torch.empty((b, h, G, topk), dtype=torch.int32, device=q.device)
     ws = _workspace(anchor_select_workspace_bytes(dims, topk), q.device, workspace)
-    st = lib().mcs_anchor_select(
-        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
-        _need(v, "v", torch.bfloat16, q.shape), _need(perm, "perm", torch.int32, (b, h, n_pad)),
-        topk, scale, _need(o_full, "o_full", torch.bfloat16, q.shape),
-        _need(lse, "lse", torch.float32, (b, h, n_pad)),
-        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)),
-        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    args = (_view(q, "q", q.shape), _view(k, "k", q.shape), _view(v, "v", q.shape),
+            _need(perm, "perm", torch.int32, (b, h, n_pad)), topk, scale,
+            _view(o_full, "o_full", q.shape), _need(lse, "lse", torch.float32, (b, h, n_pad)),
+            _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)),
+            ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    lay = layout_of(q, k, v, o_full)
+    if lay is None:
+        st = lib().mcs_anchor_select(ctypes.byref(dims), *args)
+    else:
+        st = lib().mcs_anchor_select_strided(ctypes.byref(dims), ctypes.byref(lay), *args)
     _check(st, "mcs_anchor_select")
     return o_full, lse, kv_idx
 
 
 def residual(q, k, v, perm, kv_idx, o_full, n_valid: int, group_size: int,
              scale: Optional[float] = None, r=None, stream=None) -> torch.Tensor:
-    """R = O_full - SparseAttn(Q, K, V; perm, kv_idx) (mcs_residual)."""
+    """R = O_full - SparseAttn(Q, K, V; perm, kv_idx) (mcs_residual).  q, k, v
+    and o_full may be strided views (mcs_residual_strided); R is contiguous."""
     dims = _dims_of(q, n_valid, group_size)
     b, h, n_pad, d = q.shape
     G = n_pad // group_size
     topk = kv_idx.shape[-1]
     scale = default_scale(d) if scale is None else scale
     if r is None:
-        r = torch.empty_like(q)
-    st = lib().mcs_residual(
-        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
-        _need(v, "v", torch.bfloat16, q.shape), _need(perm, "perm", torch.int32, (b, h, n_pad)),
-        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)), topk, scale,
-        _need(o_full, "o_full", torch.bfloat16, q.shape), _need(r, "r", torch.bfloat16, q.shape),
-        _stream(stream))
+        r = _contig_out(q)
+    args = (_view(q, "q", q.shape), _view(k, "k", q.shape), _view(v, "v", q.shape),
+            _need(perm, "perm", torch.int32, (b, h, n_pad)),
+            _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)), topk, scale,
+            _view(o_full, "o_full", q.shape), _need(r, "r", torch.bfloat16, q.shape),
+            _stream(stream))
+    lay = layout_of(q, k, v, o_full)
+    if lay is None:
+        st = lib().mcs_residual(ctypes.byref(dims), *args)
+    else:
+        st = lib().mcs_residual_strided(ctypes.byref(dims), ctypes.byref(lay), *args)
     _check(st, "mcs_residual")
     return r
 
@@ -212,7 +277,9 @@ def residual(q, k, v, perm, kv_idx, o_full, n_valid: int, group_size: int,
 def sparse_attn(q, k, v, perm, kv_idx, r, n_valid: int, group_size: int,
                 scale: Optional[float] = None, o=None, stream=None) -> torch.Tensor:
     """Reuse step O = SparseAttn(Q, K, V; perm, kv_idx) + R (mcs_sparse_attn).
-    `r` may be None (no residual)."""
+    `r` may be None (no residual).  q, k, v and o may be strided views
+    (mcs_sparse_attn_strided); the default o has q's layout where torch can
+    reproduce it."""
     dims = _dims_of(q, n_valid, group_size)
     b, h, n_pad, d = q.shape
     G = n_pad // group_size
@@ -221,18 +288,23 @@ def sparse_attn(q, k, v, perm, kv_idx, r, n_valid: int, group_size: int,
     if o is None:
         o = torch.empty_like(q)
     rp = None if r is None else _need(r, "r", torch.bfloat16, q.shape)
-    st = lib().mcs_sparse_attn(
-        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
-        _need(v, "v", torch.bfloat16, q.shape), _need(perm, "perm", torch.int32, (b, h, n_pad)),
-        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)), topk, scale, rp,
-        _need(o, "o", torch.bfloat16, q.shape), _stream(stream))
+    args = (_view(q, "q", q.shape), _view(k, "k", q.shape), _view(v, "v", q.shape),
+            _need(perm, "perm", torch.int32, (b, h, n_pad)),
+            _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)), topk, scale, rp,
+            _view(o, "o", q.shape), _stream(stream))
+    lay = layout_of(q, k, v, o)
+    if lay is None:
+        st = lib().mcs_sparse_attn(ctypes.byref(dims), *args)
+    else:
+        st = lib().mcs_sparse_attn_strided(ctypes.byref(dims), ctypes.byref(lay), *args)
     _check(st, "mcs_sparse_attn")
     return o
 
 
 def dense_attn(q, k, v, n_valid: int, group_size: int = 128, scale: Optional[float] = None,
                o=None, lse=None, want_lse: bool = True, stream=None):
-    """Dense attention -> (o, lse) (mcs_dense_attn)."""
+    """Dense attention -> (o, lse) (mcs_dense_attn).  q, k, v and o may be
+    strided views (mcs_dense_attn_strided)."""
     dims = _dims_of(q, n_valid, group_size)
     b, h, n_pad, d = q.shape
     scale = default_scale(d) if scale is None else scale
@@ -241,10 +313,13 @@ def dense_attn(q, k, v, n_valid: int, group_size: int = 128, scale: Optional[flo
     if lse is None and want_lse:
         lse = torch.empty((b, h, n_pad), dtype=torch.float32, device=q.device)
     lp = None if lse is None else _need(lse, "lse", torch.float32, (b, h, n_pad))
-    st = lib().mcs_dense_attn(
-        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
-        _need(v, "v", torch.bfloat16, q.shape), scale, _need(o, "o", torch.bfloat16, q.shape), lp,
-        _stream(stream))
+    args = (_view(q, "q", q.shape), _view(k, "k", q.shape), _view(v, "v", q.shape), scale,
+            _view(o, "o", q.shape), lp, _stream(stream))
+    lay = layout_of(q, k, v, o)
+    if lay is None:
+        st = lib().mcs_dense_attn(ctypes.byref(dims), *args)
+    else:
+        st = lib().mcs_dense_attn_strided(ctypes.byref(dims), ctypes.byref(lay), *args)
     _check(st, "mcs_dense_attn")
     return o, lse
 

@@ -52,10 +52,9 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = work / G;
   const int g = work - (int)(bh * G);
-  const size_t mat = (size_t)bh * p.n_pad * D;
-  const uint16_t* Qb = p.q + mat;
-  const uint16_t* Kb = p.k + mat;
-  const uint16_t* Vb = p.v + mat;
+  const uint16_t* Qb = p.q + head_offset(p.sq, bh, p.heads);
+  const uint16_t* Kb = p.k + head_offset(p.sk, bh, p.heads);
+  const uint16_t* Vb = p.v + head_offset(p.sv, bh, p.heads);
 
   // ---- query rows of this lane (B operand of S^T, resident in VGPRs) ----
   const int qpos = g * C + 32 * w + ql;
@@ -63,7 +62,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   bf16x8 qreg[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
-    qreg[kk] = *(const bf16x8*)(Qb + (size_t)qrow * D + 16 * kk + 8 * h);
+    qreg[kk] = *(const bf16x8*)(Qb + (int64_t)qrow * p.sq.n + 16 * kk + 8 * h);
 
   // keys of this group: all valid keys (dense), or the first nk indices of
   // the group's row (a per-group count, clamped to 1 .. row stride, or topk)
@@ -88,17 +87,17 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   // offset register serves all its index loads.  Any fixed order of the keys
   // inside a tile is valid, as K and V share it and only the final-tile mask
   // looks at key positions.  K, V and the index row are read through buffer
-  // resources with 32-bit offsets; reads past a resource's end return zero,
-  // which the final-tile mask covers for the index row.
+  // resources with 32-bit offsets (row * row stride, a 24-bit multiply);
+  // reads past a resource's end return zero, which the final-tile mask covers
+  // for the index row.
   constexpr int NTOK = IPW < 4 ? IPW : 4;     // distinct keys per lane per tile
-  constexpr int RSH = (D == 128) ? 8 : 7;     // log2 of the row size in bytes
   const int r0 = (w * IPW) & 3;
   const int j4 = 4 * (lane >> 2);
   const uint32_t gcb = 16u * (uint32_t)((lane ^ (lane >> 4)) & 3);
   const uint32_t plane_soff = (uint32_t)((w * IPW) >> 2) * 64u;
-  const uint32_t mat_bytes = (uint32_t)p.n_pad << RSH;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, mat_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, mat_bytes);
+  const uint32_t rsb = (uint32_t)p.sk.n * 2u;  // row stride of K and V in bytes
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, head_span_bytes(p.sk, p.n_pad, D));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, head_span_bytes(p.sv, p.n_pad, D));
   const __amdgpu_buffer_rsrc_t irs =
       (MODE == ATTN_DENSE) ? krs : make_rsrc(idxrow, (uint32_t)nk * 4u);
   int tok[NTOK];
@@ -118,7 +117,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
     char* vdst = kdst + TILE;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const uint32_t voff = ((uint32_t)tok[i % NTOK] << RSH) | gcb;
+      const uint32_t voff = __umul24((uint32_t)tok[i % NTOK], rsb) + gcb;
       gather16_buf(krs, kdst + i * 1024, voff, plane_soff + (i >> 2) * 64);
       gather16_buf(vrs, vdst + i * 1024, voff, plane_soff + (i >> 2) * 64);
     }
@@ -185,7 +184,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int c = kk * PER; c < (kk + 1) * PER && c < 2 * IPW; ++c) {
           const int i = c >> 1;
-          const uint32_t voff = ((uint32_t)tok[i % NTOK] << RSH) | gcb;
+          const uint32_t voff = __umul24((uint32_t)tok[i % NTOK], rsb) + gcb;
           if (c & 1)
             gather16_buf(vrs, kdst_n + TILE + i * 1024, voff, plane_soff + (i >> 2) * 64);
           else
@@ -277,8 +276,9 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   const float lsum = sum_xor32(lrun);
   const float inv = 1.f / lsum;
   const bool valid = qrow < p.n_valid;
-  uint16_t* Ob = p.out + mat + (size_t)qrow * D;
-  const uint16_t* Ab = (p.aux != nullptr) ? p.aux + mat + (size_t)qrow * D : nullptr;
+  uint16_t* Ob = p.out + head_offset(p.so, bh, p.heads) + (int64_t)qrow * p.so.n;
+  const uint16_t* Ab =
+      (p.aux != nullptr) ? p.aux + head_offset(p.sa, bh, p.heads) + (int64_t)qrow * p.sa.n : nullptr;
 #pragma unroll
   for (int T = 0; T < NPL; ++T) {
 #pragma unroll

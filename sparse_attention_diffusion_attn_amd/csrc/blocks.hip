@@ -50,11 +50,11 @@ __global__ __launch_bounds__(D) void key_pool_kernel(BlockParams p) {
   const int64_t bl = blockIdx.x / p.nb;
   const int b = (int)(blockIdx.x - bl * p.nb);
   const int d = threadIdx.x;
-  const uint16_t* K = p.k + (size_t)(p.bh0 + bl) * p.n_pad * D;
+  const uint16_t* K = p.k + head_offset(p.sk, p.bh0 + bl, p.heads);
   const int j0 = b * p.block;
   const int j1 = min(j0 + p.block, p.n_valid);
   double s = 0.0;
-  for (int j = j0; j < j1; ++j) s += (double)bf16_to_f32(K[(size_t)j * D + d]);
+  for (int j = j0; j < j1; ++j) s += (double)bf16_to_f32(K[(int64_t)j * p.sk.n + d]);
   double* kb = p.kbar + ((size_t)bl * p.nb + b) * D;
   kb[d] = s / (double)(j1 - j0);
 }
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void meanpool_kernel(BlockParams p) {
   const int64_t bl = blockIdx.x / G;
   const int g = (int)(blockIdx.x - bl * G);
   const int64_t bh = p.bh0 + bl;
-  const uint16_t* Q = p.q + (size_t)bh * p.n_pad * D;
+  const uint16_t* Q = p.q + head_offset(p.sq, bh, p.heads);
   const int32_t* mem = p.perm + (size_t)bh * p.n_pad + (size_t)g * C;
   const int tid = threadIdx.x, d = tid % D, pt = tid / D;
   double s = 0.0;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void meanpool_kernel(BlockParams p) {
   for (int r = pt; r < C; r += PARTS) {
     const int row = mem[r];
     if (row < p.n_valid) {
-      s += (double)bf16_to_f32(Q[(size_t)row * D + d]);
+      s += (double)bf16_to_f32(Q[(int64_t)row * p.sq.n + d]);
       ++cnt;
     }
   }

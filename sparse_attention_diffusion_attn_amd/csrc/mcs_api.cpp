@@ -100,6 +100,94 @@ int32_t hip_status(hipError_t e, const char* what) {
     if (_st != MCS_OK) return _st; \
   } while (0)
 
+// ---- tensor layouts ----
+// Strides of q, k, v and the layer output (o / o_full) in the kernels' form.
+struct Lay {
+  mcs::Strides q, k, v, o;
+};
+
+mcs::Strides bhnd_strides(const mcs_dims* d) {
+  return {(int64_t)d->heads * d->n_pad * d->head_dim, (int64_t)d->n_pad * d->head_dim,
+          (int64_t)d->head_dim};
+}
+
+// A stride of a dimension of extent 1 is never used; it is taken as 0.
+mcs_strides used_strides(const mcs_dims* d, mcs_strides s) {
+  if (d->batch == 1) s.batch = 0;
+  if (d->heads == 1) s.head = 0;
+  if (d->n_pad == 1) s.token = 0;
+  return s;
+}
+
+mcs::Strides to_strides(const mcs_strides& s) { return {s.batch, s.head, s.token}; }
+
+int32_t check_strides(const mcs_dims* d, const mcs_strides& s, const char* name, bool written) {
+  const int64_t st[3] = {s.batch, s.head, s.token};
+  const int64_t ext[3] = {d->batch, d->heads, d->n_pad};
+  static const char* what[3] = {"batch", "head", "token"};
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0 || st[i] >= ((int64_t)1 << 40))
+      return fail(MCS_ERR_INVALID_ARG, "%s %s stride %lld outside 0 .. 2^40 - 1", name, what[i],
+                  (long long)st[i]);
+    if (st[i] % 8 != 0)
+      return fail(MCS_ERR_INVALID_ARG, "%s %s stride %lld is not a multiple of 8 elements", name,
+                  what[i], (long long)st[i]);
+  }
+  if (s.token >= ((int64_t)1 << 23))
+    return fail(MCS_ERR_UNSUPPORTED, "%s token stride %lld too large (< 2^23)", name,
+                (long long)s.token);
+  // a head's rows are read through 32-bit byte offsets
+  if (((__int128)(d->n_pad - 1) * s.token + d->head_dim) * 2 > (__int128)0xffffffffu)
+    return fail(MCS_ERR_UNSUPPORTED, "%s: one head's rows span 4 GiB or more", name);
+  __int128 reach = d->head_dim;
+  for (int i = 0; i < 3; ++i) reach += (__int128)(ext[i] - 1) * st[i];
+  if (reach >= ((__int128)1 << 40))
+    return fail(MCS_ERR_UNSUPPORTED, "%s spans 2^40 elements or more", name);
+  if (written) {
+    // rows of an output must not overlap: order the dimensions of extent > 1
+    // by stride; each must step over everything the smaller ones cover
+    int64_t ss[3], ee[3];
+    int n = 0;
+    for (int i = 0; i < 3; ++i)
+      if (ext[i] > 1) { ss[n] = st[i]; ee[n] = ext[i]; ++n; }
+    for (int i = 1; i < n; ++i)
+      for (int j = i; j > 0 && ss[j] < ss[j - 1]; --j) {
+        std::swap(ss[j], ss[j - 1]);
+        std::swap(ee[j], ee[j - 1]);
+      }
+    __int128 covered = d->head_dim;
+    for (int i = 0; i < n; ++i) {
+      if ((__int128)ss[i] < covered)
+        return fail(MCS_ERR_INVALID_ARG, "%s rows overlap (strides %lld/%lld/%lld)", name,
+                    (long long)s.batch, (long long)s.head, (long long)s.token);
+      covered = (__int128)ss[i] * ee[i];
+    }
+  }
+  return MCS_OK;
+}
+
+// NULL = every tensor contiguous [B, H, n_pad, d].
+int32_t resolve_layout(const mcs_dims* d, const mcs_layout* l, Lay* out) {
+  if (l == nullptr) {
+    out->q = out->k = out->v = out->o = bhnd_strides(d);
+    return MCS_OK;
+  }
+  const mcs_strides q = used_strides(d, l->q), k = used_strides(d, l->k);
+  const mcs_strides v = used_strides(d, l->v), o = used_strides(d, l->o);
+  MCS_TRY(check_strides(d, q, "q", false));
+  MCS_TRY(check_strides(d, k, "k", false));
+  MCS_TRY(check_strides(d, v, "v", false));
+  MCS_TRY(check_strides(d, o, "o", true));
+  if (k.token != v.token)
+    return fail(MCS_ERR_UNSUPPORTED, "k and v must share the token stride (%lld vs %lld)",
+                (long long)k.token, (long long)v.token);
+  out->q = to_strides(q);
+  out->k = to_strides(k);
+  out->v = to_strides(v);
+  out->o = to_strides(o);
+  return MCS_OK;
+}
+
 // ---- workspace layouts ----
 struct GroupWs {
   size_t partial, mu, vec, proj, perm, total;
@@ -170,7 +258,8 @@ int32_t attn_varlen(int mode, const mcs_dims* dims, const uint16_t* q, const uin
   mcs::AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.kv_count = kv_count;
   p.aux = aux; p.out = out;
-  p.bh = (int64_t)dims->batch * dims->heads;
+  p.sq = p.sk = p.sv = p.so = p.sa = bhnd_strides(dims);
+  p.bh = (int64_t)dims->batch * dims->heads; p.heads = dims->heads;
   p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
   p.groups = dims->n_pad / dims->group_size; p.topk = kv_stride; p.kv_stride = kv_stride;
   p.scale = scale;
@@ -183,6 +272,20 @@ int32_t attn_varlen(int mode, const mcs_dims* dims, const uint16_t* q, const uin
 extern "C" {
 
 int32_t mcs_abi_version(void) { return MCS_ABI_VERSION; }
+
+void mcs_layout_bhnd(const mcs_dims* dims, mcs_layout* layout) {
+  if (dims == nullptr || layout == nullptr) return;
+  const int64_t d = dims->head_dim, n = dims->n_pad, h = dims->heads;
+  const mcs_strides s = {h * n * d, n * d, d};
+  *layout = {s, s, s, s};
+}
+
+void mcs_layout_bnhd(const mcs_dims* dims, mcs_layout* layout) {
+  if (dims == nullptr || layout == nullptr) return;
+  const int64_t d = dims->head_dim, n = dims->n_pad, h = dims->heads;
+  const mcs_strides s = {n * h * d, d, h * d};
+  *layout = {s, s, s, s};
+}
 
 const char* mcs_status_string(int32_t s) {
   switch (s) {
@@ -205,7 +308,16 @@ size_t mcs_group_workspace_bytes(const mcs_dims* dims) {
 int32_t mcs_group(const mcs_dims* dims, const uint16_t* q, int32_t power_iters,
                   int32_t max_levels, int32_t* perm, void* workspace, size_t workspace_bytes,
                   void* stream) {
+  return mcs_group_strided(dims, nullptr, q, power_iters, max_levels, perm, workspace,
+                           workspace_bytes, stream);
+}
+
+int32_t mcs_group_strided(const mcs_dims* dims, const mcs_layout* layout, const uint16_t* q,
+                          int32_t power_iters, int32_t max_levels, int32_t* perm, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   MCS_TRY(check_dims(dims));
+  Lay lay;
+  MCS_TRY(resolve_layout(dims, layout, &lay));
   MCS_TRY(check_ptr(q, "q"));
   MCS_TRY(check_ptr(perm, "perm"));
   if (power_iters < 0 || power_iters > 1000)
@@ -233,7 +345,9 @@ int32_t mcs_group(const mcs_dims* dims, const uint16_t* q, int32_t power_iters,
   p.mu = (double*)(ws + w.mu);
   p.vec = (double*)(ws + w.vec);
   p.proj = (double*)(ws + w.proj);
+  p.sq = lay.q;
   p.bh = (int64_t)dims->batch * dims->heads;
+  p.heads = dims->heads;
   p.n_pad = dims->n_pad;
   p.groups = G;
   p.perm_cur = bufs[cur];
@@ -271,16 +385,26 @@ size_t mcs_anchor_select_min_workspace_bytes(const mcs_dims* dims, int32_t topk)
 
 int32_t mcs_dense_attn(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, float scale, uint16_t* o, float* lse, void* stream) {
+  return mcs_dense_attn_strided(dims, nullptr, q, k, v, scale, o, lse, stream);
+}
+
+int32_t mcs_dense_attn_strided(const mcs_dims* dims, const mcs_layout* layout, const uint16_t* q,
+                               const uint16_t* k, const uint16_t* v, float scale, uint16_t* o,
+                               float* lse, void* stream) {
   MCS_TRY(check_dims(dims));
+  Lay lay;
+  MCS_TRY(resolve_layout(dims, layout, &lay));
   MCS_TRY(check_ptr(q, "q"));
   MCS_TRY(check_ptr(k, "k"));
   MCS_TRY(check_ptr(v, "v"));
   MCS_TRY(check_ptr(o, "o"));
   MCS_TRY(check_ptr(lse, "lse", true));
   MCS_TRY(check_scale(scale));
+  if (o == q || o == k || o == v) return fail(MCS_ERR_INVALID_ARG, "o must not alias q, k or v");
   mcs::AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.out = o; p.lse = lse;
-  p.bh = (int64_t)dims->batch * dims->heads;
+  p.sq = lay.q; p.sk = lay.k; p.sv = lay.v; p.so = lay.o; p.sa = lay.o;
+  p.bh = (int64_t)dims->batch * dims->heads; p.heads = dims->heads;
   p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
   p.groups = dims->n_pad / dims->group_size;
   p.scale = scale;
@@ -294,7 +418,18 @@ int32_t mcs_anchor_select(const mcs_dims* dims, const uint16_t* q, const uint16_
                           const uint16_t* v, const int32_t* perm, int32_t topk, float scale,
                           uint16_t* o_full, float* lse, int32_t* kv_idx, void* workspace,
                           size_t workspace_bytes, void* stream) {
+  return mcs_anchor_select_strided(dims, nullptr, q, k, v, perm, topk, scale, o_full, lse, kv_idx,
+                                   workspace, workspace_bytes, stream);
+}
+
+int32_t mcs_anchor_select_strided(const mcs_dims* dims, const mcs_layout* layout,
+                                  const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const int32_t* perm, int32_t topk, float scale, uint16_t* o_full,
+                                  float* lse, int32_t* kv_idx, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   MCS_TRY(check_dims(dims));
+  Lay lay;
+  MCS_TRY(resolve_layout(dims, layout, &lay));
   MCS_TRY(check_ptr(q, "q"));
   MCS_TRY(check_ptr(k, "k"));
   MCS_TRY(check_ptr(v, "v"));
@@ -304,6 +439,8 @@ int32_t mcs_anchor_select(const mcs_dims* dims, const uint16_t* q, const uint16_
   MCS_TRY(check_ptr(kv_idx, "kv_idx"));
   MCS_TRY(check_topk(dims, topk));
   MCS_TRY(check_scale(scale));
+  if (o_full == q || o_full == k || o_full == v)
+    return fail(MCS_ERR_INVALID_ARG, "o_full must not alias q, k or v");
   const size_t per_head = scores_per_head(dims);
   if (workspace == nullptr || workspace_bytes < per_head)
     return fail(MCS_ERR_WORKSPACE, "workspace needs at least %zu bytes, got %zu", per_head,
@@ -317,7 +454,9 @@ int32_t mcs_anchor_select(const mcs_dims* dims, const uint16_t* q, const uint16_
   // pass 1: dense attention (O_full, lse)
   mcs::AttnParams a{};
   a.q = q; a.k = k; a.v = v; a.out = o_full; a.lse = lse;
-  a.bh = bh; a.n_valid = dims->n_valid; a.n_pad = dims->n_pad; a.groups = G; a.scale = scale;
+  a.sq = lay.q; a.sk = lay.k; a.sv = lay.v; a.so = lay.o; a.sa = lay.o;
+  a.bh = bh; a.heads = dims->heads;
+  a.n_valid = dims->n_valid; a.n_pad = dims->n_pad; a.groups = G; a.scale = scale;
   MCS_TRY(hip_status(mcs::launch_attention(mcs::ATTN_DENSE, dims->head_dim, dims->group_size, a, s),
                      "anchor pass 1"));
 
@@ -330,6 +469,7 @@ int32_t mcs_anchor_select(const mcs_dims* dims, const uint16_t* q, const uint16_
     mcs::ScoreParams sp{};
     sp.q = q; sp.k = k; sp.perm = perm; sp.lse = lse; sp.scores = (float*)workspace;
     sp.hist = hist;
+    sp.sq = lay.q; sp.sk = lay.k; sp.heads = dims->heads;
     sp.bh0 = h0; sp.bh_count = hc; sp.n_valid = dims->n_valid; sp.n_pad = dims->n_pad;
     sp.groups = G; sp.scale = scale;
     MCS_TRY(hip_status(mcs::launch_scores(dims->head_dim, dims->group_size, sp, s), "anchor pass 2"));
@@ -358,12 +498,32 @@ static int32_t sparse_common(const mcs_dims* dims, const uint16_t* q, const uint
 int32_t mcs_residual(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
                      const uint16_t* v, const int32_t* perm, const int32_t* kv_idx, int32_t topk,
                      float scale, const uint16_t* o_full, uint16_t* r, void* stream) {
+  return mcs_residual_strided(dims, nullptr, q, k, v, perm, kv_idx, topk, scale, o_full, r,
+                              stream);
+}
+
+int32_t mcs_residual_strided(const mcs_dims* dims, const mcs_layout* layout, const uint16_t* q,
+                             const uint16_t* k, const uint16_t* v, const int32_t* perm,
+                             const int32_t* kv_idx, int32_t topk, float scale,
+                             const uint16_t* o_full, uint16_t* r, void* stream) {
   MCS_TRY(sparse_common(dims, q, k, v, perm, kv_idx, topk, scale));
+  Lay lay;
+  MCS_TRY(resolve_layout(dims, layout, &lay));
   MCS_TRY(check_ptr(o_full, "o_full"));
   MCS_TRY(check_ptr(r, "r"));
+  const mcs::Strides rs = bhnd_strides(dims);
+  if (r == q || r == k || r == v)
+    return fail(MCS_ERR_INVALID_ARG, "r must not alias q, k or v");
+  // R may overwrite O_full in place (every element is read, then written, by
+  // the same lane) only if both have the same layout
+  const mcs_strides ru = used_strides(dims, {rs.b, rs.h, rs.n});
+  const mcs_strides ou = used_strides(dims, {lay.o.b, lay.o.h, lay.o.n});
+  if (r == o_full && (ou.batch != ru.batch || ou.head != ru.head || ou.token != ru.token))
+    return fail(MCS_ERR_INVALID_ARG, "r may alias o_full only if o_full is contiguous");
   mcs::AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.aux = o_full; p.out = r;
-  p.bh = (int64_t)dims->batch * dims->heads;
+  p.sq = lay.q; p.sk = lay.k; p.sv = lay.v; p.so = rs; p.sa = lay.o;
+  p.bh = (int64_t)dims->batch * dims->heads; p.heads = dims->heads;
   p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
   p.groups = dims->n_pad / dims->group_size; p.topk = topk; p.kv_stride = topk; p.scale = scale;
   MCS_TRY(hip_status(mcs::launch_attention(mcs::ATTN_RESID, dims->head_dim, dims->group_size, p,
@@ -375,14 +535,24 @@ int32_t mcs_residual(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
 int32_t mcs_sparse_attn(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const int32_t* perm, const int32_t* kv_idx,
                         int32_t topk, float scale, const uint16_t* r, uint16_t* o, void* stream) {
+  return mcs_sparse_attn_strided(dims, nullptr, q, k, v, perm, kv_idx, topk, scale, r, o, stream);
+}
+
+int32_t mcs_sparse_attn_strided(const mcs_dims* dims, const mcs_layout* layout,
+                                const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* perm, const int32_t* kv_idx, int32_t topk,
+                                float scale, const uint16_t* r, uint16_t* o, void* stream) {
   MCS_TRY(sparse_common(dims, q, k, v, perm, kv_idx, topk, scale));
+  Lay lay;
+  MCS_TRY(resolve_layout(dims, layout, &lay));
   MCS_TRY(check_ptr(r, "r", true));
   MCS_TRY(check_ptr(o, "o"));
   if (o == q || o == k || o == v || (r != nullptr && o == r))
     return fail(MCS_ERR_INVALID_ARG, "o must not alias q, k, v or r");
   mcs::AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.perm = perm; p.kv_idx = kv_idx; p.aux = r; p.out = o;
-  p.bh = (int64_t)dims->batch * dims->heads;
+  p.sq = lay.q; p.sk = lay.k; p.sv = lay.v; p.so = lay.o; p.sa = bhnd_strides(dims);
+  p.bh = (int64_t)dims->batch * dims->heads; p.heads = dims->heads;
   p.n_valid = dims->n_valid; p.n_pad = dims->n_pad;
   p.groups = dims->n_pad / dims->group_size; p.topk = topk; p.kv_stride = topk; p.scale = scale;
   MCS_TRY(hip_status(mcs::launch_attention(mcs::ATTN_SPARSE, dims->head_dim, dims->group_size, p,
@@ -440,12 +610,14 @@ int32_t mcs_block_select(const mcs_dims* dims, const uint16_t* q, const uint16_t
     bp.block_scores = (float*)(ws + rs + rk);
     bp.block_idx = (const int32_t*)(ws + rs + rk + rb);
     bp.kv_idx = kv_idx; bp.kv_count = kv_count;
+    bp.sq = bp.sk = bhnd_strides(dims); bp.heads = dims->heads;
     bp.bh0 = h0; bp.bh_count = hc;
     bp.n_valid = dims->n_valid; bp.n_pad = dims->n_pad; bp.groups = G;
     bp.block = block; bp.nb = nb; bp.nblocks = nblocks; bp.scale = scale;
     if (mode == MCS_BLOCK_EXACT) {
       mcs::ScoreParams sp{};
       sp.q = q; sp.k = k; sp.perm = perm; sp.lse = lse; sp.scores = (float*)ws;
+      sp.sq = sp.sk = bhnd_strides(dims); sp.heads = dims->heads;
       sp.bh0 = h0; sp.bh_count = hc; sp.n_valid = dims->n_valid; sp.n_pad = dims->n_pad;
       sp.groups = G; sp.scale = scale;
       MCS_TRY(hip_status(mcs::launch_scores(dims->head_dim, dims->group_size, sp, s), "block scores pass"));

@@ -9,6 +9,26 @@ namespace mcs {
 
 enum AttnMode : int { ATTN_DENSE = 0, ATTN_SPARSE = 1, ATTN_RESID = 2 };
 
+// Element strides of a bf16 tensor viewed as [batch, heads, n_pad, d] whose
+// rows (d values) are contiguous: row (b, h, n) starts at element
+// b*s.b + h*s.h + n*s.n.  The C-ABI layer checks that every stride keeps rows
+// 16-byte aligned and that a head's rows span less than 4 GiB (the reach of a
+// buffer resource).
+struct Strides {
+  int64_t b, h, n;
+};
+
+// Element offset of head bh = b*heads + h (bh < 2^31).
+__host__ __device__ __forceinline__ int64_t head_offset(const Strides& s, int64_t bh, int32_t heads) {
+  const int32_t b = (int32_t)bh / heads;
+  return (int64_t)b * s.b + (int64_t)((int32_t)bh - b * heads) * s.h;
+}
+
+// Bytes from a head's first row to the end of row n_pad - 1.
+__host__ __device__ __forceinline__ uint32_t head_span_bytes(const Strides& s, int32_t n_pad, int d) {
+  return (uint32_t)(((int64_t)(n_pad - 1) * s.n + d) * 2);
+}
+
 struct AttnParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -19,7 +39,10 @@ struct AttnParams {
   const uint16_t* aux;    // sparse: residual to add (nullable); resid: O_full
   uint16_t* out;          // O (dense, sparse) or R (resid)
   float* lse;             // dense: nullable
+  Strides sq, sk, sv;     // q, k, v (k and v share the token stride)
+  Strides so, sa;         // out, aux
   int64_t bh;             // batch * heads
+  int32_t heads;
   int32_t n_valid, n_pad, groups, topk;
   int32_t kv_stride;      // row stride of kv_idx (>= every count)
   float scale;
@@ -32,7 +55,9 @@ struct ScoreParams {
   const float* lse;
   float* scores;          // [bh_count, G, n_valid]
   int32_t* hist;          // [bh_count, G, 1024] top-10-bit histogram of each row, or NULL
+  Strides sq, sk;
   int64_t bh0, bh_count;  // heads [bh0, bh0 + bh_count)
+  int32_t heads;
   int32_t n_valid, n_pad, groups;
   float scale;
 };
@@ -59,7 +84,9 @@ struct BlockParams {
   const int32_t* block_idx;   // expansion: [bh_count, G, nblocks], ascending
   int32_t* kv_idx;            // expansion: [BH, G, nblocks*block] tokens
   int32_t* kv_count;          // expansion: [BH, G]
+  Strides sq, sk;
   int64_t bh0, bh_count;
+  int32_t heads;
   int32_t n_valid, n_pad, groups, block, nb, nblocks;
   float scale;
 };
@@ -72,7 +99,9 @@ struct PddpParams {
   double* mu;             // [BH, G, d]  indexed by node start group
   double* vec;            // [BH, G, d]
   double* proj;           // [BH, n_pad] by position
+  Strides sq;
   int64_t bh;
+  int32_t heads;
   int32_t n_pad, groups, level;
   int32_t fix_sign;       // reduce stage 1: apply the sign rule to v (last power step)
 };

@@ -155,9 +155,9 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   // this thread's 8 bf16 of each of its rows (16 bytes each)
   auto load_rows = [&](int64_t b, const int (&ix)[RPT], uint4 (&xr)[RPT]) {
     const int64_t bh = b / G;
-    const uint16_t* Qb = p.q + bh * p.n_pad * D;
+    const uint16_t* Qb = p.q + head_offset(p.sq, bh, p.heads);
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) xr[k] = *(const uint4*)(Qb + (int64_t)ix[k] * D + 8 * dg);
+    for (int k = 0; k < RPT; ++k) xr[k] = *(const uint4*)(Qb + (int64_t)ix[k] * p.sq.n + 8 * dg);
   };
   // mu and v of block b's node into LDS half `buf` (one 16-byte copy per lane
   // of waves 0 and 1; for D = 64 the upper half of the copy is not used)

@@ -45,9 +45,8 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
   const int64_t bl = work / G;               // head within this chunk
   const int g = work - (int)(bl * G);
   const int64_t bh = p.bh0 + bl;
-  const size_t mat = (size_t)bh * p.n_pad * D;
-  const uint16_t* Qb = p.q + mat;
-  const uint16_t* Kb = p.k + mat;
+  const uint16_t* Qb = p.q + head_offset(p.sq, bh, p.heads);
+  const uint16_t* Kb = p.k + head_offset(p.sk, bh, p.heads);
   const int32_t* permb = p.perm + (size_t)bh * p.n_pad + (size_t)g * C;
 
   // A operand of S = Q K^T: this lane's query row 32w + ql.
@@ -55,7 +54,7 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
   bf16x8 qreg[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
-    qreg[kk] = *(const bf16x8*)(Qb + (size_t)qrow * D + 16 * kk + 8 * h);
+    qreg[kk] = *(const bf16x8*)(Qb + (int64_t)qrow * p.sq.n + 16 * kk + 8 * h);
 
   // Accumulator j of S holds query 32w + 8(j/4) + 4h + (j%4): its lse in log2
   // units (+inf for padded queries, whose terms then vanish).
@@ -70,18 +69,18 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
   const int ntiles = (nk + KT - 1) / KT;
   // Copy instruction ins = w*IPW + i fills plane ins/4, rows 16*(ins%4) + l/4
   // (lane l), physical chunk l%4 = logical chunk (l%4)^((l/16)%4); rows are
-  // read through a buffer resource with 32-bit offsets, the per-instruction
-  // part of the offset in a scalar register.
-  constexpr int RSH = (D == 128) ? 8 : 7;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, (uint32_t)p.n_pad << RSH);
-  const uint32_t lane_off = ((uint32_t)(lane >> 2) << RSH) | (16u * (uint32_t)((lane ^ (lane >> 4)) & 3));
+  // read through a buffer resource with 32-bit offsets (row * row stride),
+  // the per-instruction part of the offset in a scalar register.
+  const uint32_t rsb = (uint32_t)p.sk.n * 2u;  // row stride of K in bytes
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, head_span_bytes(p.sk, p.n_pad, D));
+  const uint32_t lane_off = (uint32_t)(lane >> 2) * rsb + 16u * (uint32_t)((lane ^ (lane >> 4)) & 3);
   auto issue = [&](int t, int buf) {
     char* kdst = lds + buf * TILE + w * IPW * 1024;
-    const uint32_t voff = ((uint32_t)(t * KT) << RSH) + lane_off;
+    const uint32_t voff = (uint32_t)(t * KT) * rsb + lane_off;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int ins = w * IPW + i;
-      const uint32_t soff = ((uint32_t)(16 * (ins & 3)) << RSH) + 64u * (uint32_t)(ins >> 2);
+      const uint32_t soff = (uint32_t)(16 * (ins & 3)) * rsb + 64u * (uint32_t)(ins >> 2);
       gather16_buf(krs, kdst + i * 1024, voff, soff);
     }
   };
@@ -121,7 +120,7 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
     // the copies of tile t+1 are spread over the k-steps of tile t
     const bool more = t + 1 < ntiles;
     char* kdst_n = lds + ((t + 1) & 1) * TILE + w * IPW * 1024;
-    const uint32_t voff_n = ((uint32_t)((t + 1) * KT) << RSH) + lane_off;
+    const uint32_t voff_n = (uint32_t)((t + 1) * KT) * rsb + lane_off;
     const char* kbuf = lds + (t & 1) * TILE;
     f32x16 s0, s1;
 #pragma unroll
@@ -138,7 +137,7 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
 #pragma unroll
         for (int i = kk * PER; i < (kk + 1) * PER && i < IPW; ++i) {
           const int ins = w * IPW + i;
-          const uint32_t soff = ((uint32_t)(16 * (ins & 3)) << RSH) + 64u * (uint32_t)(ins >> 2);
+          const uint32_t soff = (uint32_t)(16 * (ins & 3)) * rsb + 64u * (uint32_t)(ins >> 2);
           gather16_buf(krs, kdst_n + i * 1024, voff_n, soff);
         }
       }

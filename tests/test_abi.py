@@ -28,7 +28,7 @@ def test_library_exports_every_header_symbol():
                           "mcs_status_string", "mcs_last_error", "mcs_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mcs_abi_version() == 1
+    assert lib.mcs_abi_version() == 2
     assert lib.mcs_status_string(3) == b"MCS_ERR_WORKSPACE"
     assert lib.mcs_status_string(99) == b"MCS_ERR_UNKNOWN"
 
@@ -111,7 +111,7 @@ def test_workspace_checks():
     assert lib.mcs_group(b, P, 20, -1, P, P + 16, need, None) == mcs.MCS_ERR_WORKSPACE
     assert "256-byte" in err()
     mn = lib.mcs_anchor_select_min_workspace_bytes(b, 5)
-    assert lib.mcs_anchor_select(b, P, P, P, P, 5, 0.1, P, P, P, P, mn - 1, None) == mcs.MCS_ERR_WORKSPACE
+    assert lib.mcs_anchor_select(b, P, P, P, P, 5, 0.1, P + 256, P, P, P, mn - 1, None) == mcs.MCS_ERR_WORKSPACE
 
 
 def test_binding_refuses_host_tensors():
@@ -153,4 +153,91 @@ def test_counts_calls_checks():
     assert lib.mcs_residual_counts(b, P, P, P, P, P, 8, P, 0.1, None, P + 256, None) == mcs.MCS_ERR_INVALID_ARG
     assert "o_full" in err()
     assert lib.mcs_sparse_attn_counts(b, P, P, P, P, P, 8, P, 0.1, None, P, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "alias" in err()
+
+
+def _layout(fn, dm):
+    lay = mcs.Layout()
+    fn(ctypes.byref(dm), ctypes.byref(lay))
+    return lay
+
+
+def test_layout_helpers():
+    lib = mcs.lib()
+    dm = d(batch=2, heads=3, n_pad=1024, head_dim=64)
+    a = _layout(lib.mcs_layout_bhnd, dm)
+    b = _layout(lib.mcs_layout_bnhd, dm)
+    for t in (a.q, a.k, a.v, a.o):
+        assert (t.batch, t.head, t.token) == (3 * 1024 * 64, 1024 * 64, 64)
+    for t in (b.q, b.k, b.v, b.o):
+        assert (t.batch, t.head, t.token) == (1024 * 3 * 64, 64, 3 * 64)
+
+
+def test_strided_layout_checks():
+    """Every bad layout is refused before anything is enqueued."""
+    lib = mcs.lib()
+    dm = d(batch=2, heads=3)
+    b = ctypes.byref(dm)
+
+    def calls(lay):
+        lp = ctypes.byref(lay)
+        return [
+            lambda: lib.mcs_group_strided(b, lp, P, 20, -1, P, P, 1 << 30, None),
+            lambda: lib.mcs_anchor_select_strided(b, lp, P, P, P, P, 5, 0.1, P + 256, P, P, P,
+                                                  1 << 30, None),
+            lambda: lib.mcs_residual_strided(b, lp, P, P, P, P, P, 5, 0.1, P, P + 256, None),
+            lambda: lib.mcs_sparse_attn_strided(b, lp, P, P, P, P, P, 5, 0.1, None, P + 256, None),
+            lambda: lib.mcs_dense_attn_strided(b, lp, P, P, P, 0.1, P + 256, None, None),
+        ]
+
+    def bad(mutate, code, msg, only=None):
+        lay = _layout(lib.mcs_layout_bnhd, dm)
+        mutate(lay)
+        cs = calls(lay)
+        for c in (cs if only is None else [cs[i] for i in only]):
+            assert c() == code, msg
+            assert msg in err()
+
+    def set_(name, field, value):
+        return lambda lay: setattr(getattr(lay, name), field, value)
+
+    bad(set_("q", "token", 3 * 128 + 4), mcs.MCS_ERR_INVALID_ARG, "multiple of 8")
+    bad(set_("q", "head", -128), mcs.MCS_ERR_INVALID_ARG, "outside")
+    bad(set_("k", "batch", 1 << 41), mcs.MCS_ERR_INVALID_ARG, "outside", only=[1, 2, 3, 4])
+    bad(set_("k", "token", 1 << 23), mcs.MCS_ERR_UNSUPPORTED, "token stride", only=[1, 2, 3, 4])
+    # one head's rows must fit a 32-bit byte offset: 1023 rows of 2^22 elements
+    bad(set_("v", "token", 1 << 22), mcs.MCS_ERR_UNSUPPORTED, "4 GiB", only=[1, 2, 3, 4])
+    bad(set_("v", "token", 3 * 128 * 2), mcs.MCS_ERR_UNSUPPORTED, "share the token stride",
+        only=[1, 2, 3, 4])
+    # overlapping output rows (token stride below the row length, or heads on top of each other)
+    bad(set_("o", "token", 64), mcs.MCS_ERR_INVALID_ARG, "overlap", only=[1, 2, 3, 4])
+    bad(set_("o", "head", 0), mcs.MCS_ERR_INVALID_ARG, "overlap", only=[1, 2, 3, 4])
+    bad(set_("o", "batch", 1024 * 3 * 128 - 8), mcs.MCS_ERR_INVALID_ARG, "overlap",
+        only=[1, 2, 3, 4])
+
+
+def test_strided_extent_one_strides_ignored_and_alias_rules():
+    """A stride of a dimension of extent 1 is not checked; R may overwrite
+    O_full only when O_full is contiguous."""
+    lib = mcs.lib()
+    dm = d(batch=1, heads=2)
+    b = ctypes.byref(dm)
+    lay = _layout(lib.mcs_layout_bnhd, dm)
+    lay.q.batch = 3           # extent 1: ignored ...
+    lay.q.token = 3           # ... but this one is not
+    assert lib.mcs_dense_attn_strided(b, ctypes.byref(lay), P, P, P, 0.1, P + 256, None,
+                                      None) == mcs.MCS_ERR_INVALID_ARG
+    assert "q token stride" in err()
+    lay = _layout(lib.mcs_layout_bnhd, dm)
+    assert lib.mcs_residual_strided(b, ctypes.byref(lay), P, P, P, P, P, 5, 0.1, P + 256,
+                                    P + 256, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "o_full is contiguous" in err()
+    assert lib.mcs_residual_strided(b, ctypes.byref(lay), P, P, P, P, P, 5, 0.1, P + 256,
+                                    P, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "alias" in err()
+    assert lib.mcs_anchor_select_strided(b, ctypes.byref(lay), P, P, P, P, 5, 0.1, P, P, P, P,
+                                         1 << 30, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "alias" in err()
+    assert lib.mcs_dense_attn_strided(b, ctypes.byref(lay), P, P, P, 0.1, P, None,
+                                      None) == mcs.MCS_ERR_INVALID_ARG
     assert "alias" in err()
