@@ -75,6 +75,8 @@ _SIGNATURES = {
     "mcs_block_select": (_I, [_DP, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _SZ, _P]),
     "mcs_sparse_attn_counts": (_I, [_DP, _P, _P, _P, _P, _P, _I, _P, _F, _P, _P, _P]),
     "mcs_residual_counts": (_I, [_DP, _P, _P, _P, _P, _P, _I, _P, _F, _P, _P, _P]),
+    "mcs_group_kmeans_workspace_bytes": (_SZ, [_DP]),
+    "mcs_group_kmeans": (_I, [_DP, _P, _I, _P, _P, _P, _SZ, _P]),
     "mcs_layout_bhnd": (None, [_DP, _LP]),
     "mcs_layout_bnhd": (None, [_DP, _LP]),
     "mcs_group_strided": (_I, [_DP, _LP, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -212,6 +214,29 @@ def group(q: torch.Tensor, n_valid: int, group_size: int, power_iters: int = 20,
                                      max_levels, pp, wsp, wsn, _stream(stream))
     _check(st, "mcs_group")
     return perm
+
+
+def group_kmeans(q: torch.Tensor, n_valid: int, group_size: int, iters: int = 10,
+                 perm: Optional[torch.Tensor] = None, labels: Optional[torch.Tensor] = None,
+                 want_labels: bool = False, workspace: Optional[torch.Tensor] = None,
+                 stream=None):
+    """Size-balanced k-means grouping, the comparator of Fast PDDP
+    (mcs_group_kmeans) -> perm int32 [B, H, n_pad], or (perm, labels) with
+    want_labels (the last iteration's nearest centroid of every token)."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    if perm is None:
+        perm = torch.empty((b, h, n_pad), dtype=torch.int32, device=q.device)
+    if labels is None and want_labels:
+        labels = torch.empty((b, h, n_pad), dtype=torch.int32, device=q.device)
+    lp = None if labels is None else _need(labels, "labels", torch.int32, (b, h, n_pad))
+    nbytes = int(lib().mcs_group_kmeans_workspace_bytes(ctypes.byref(dims)))
+    ws = _workspace(nbytes, q.device, workspace)
+    st = lib().mcs_group_kmeans(ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), iters,
+                                _need(perm, "perm", torch.int32, (b, h, n_pad)), lp,
+                                ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "mcs_group_kmeans")
+    return (perm, labels) if want_labels else perm
 
 
 def _contig_out(q: torch.Tensor) -> torch.Tensor:

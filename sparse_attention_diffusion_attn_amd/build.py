@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmcs.so")
-SOURCES = ["attn.hip", "select.hip", "pddp.hip", "blocks.hip", "mcs_api.cpp"]
+SOURCES = ["attn.hip", "select.hip", "pddp.hip", "blocks.hip", "kmeans.hip", "mcs_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -207,6 +207,34 @@ GroupWs group_ws(const mcs_dims* d) {
   return w;
 }
 
+// ---- size-balanced k-means grouping ----
+int32_t check_kmeans(const mcs_dims* d) {
+  const int G = d->n_pad / d->group_size;
+  if (G > mcs::KM_MAX_GROUPS)
+    return fail(MCS_ERR_UNSUPPORTED, "k-means grouping supports up to %d groups per head (got %d)",
+                mcs::KM_MAX_GROUPS, G);
+  return MCS_OK;
+}
+
+struct KmWs {
+  size_t perm, labels, cent, cnorm, counts, total;
+};
+
+KmWs km_ws(const mcs_dims* d) {
+  const size_t bh = (size_t)d->batch * d->heads;
+  const size_t G = (size_t)(d->n_pad / d->group_size);
+  const size_t tiles = (size_t)((d->n_pad + mcs::KM_TILE - 1) / mcs::KM_TILE);
+  KmWs w;
+  size_t o = 0;
+  w.perm = o;   o = align256(o + bh * (size_t)d->n_pad * sizeof(int32_t));
+  w.labels = o; o = align256(o + bh * (size_t)d->n_pad * sizeof(int32_t));
+  w.cent = o;   o = align256(o + bh * G * d->head_dim * sizeof(uint16_t));
+  w.cnorm = o;  o = align256(o + bh * G * sizeof(float));
+  w.counts = o; o = align256(o + bh * tiles * G * sizeof(int32_t));
+  w.total = o;
+  return w;
+}
+
 // per head: the group scores [G, n_valid] fp32, then the top-10-bit histogram
 // of each group's row [G, 1024] int32 written by the score pass
 size_t scores_bytes(const mcs_dims* d) {
@@ -368,6 +396,61 @@ int32_t mcs_group_strided(const mcs_dims* dims, const mcs_layout* layout, const 
     p.fix_sign = 0;
     MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 2, p, s), "pddp projection"));
     MCS_TRY(hip_status(mcs::launch_pddp_split(c, p, s), "pddp split"));
+    cur = 1 - cur;
+  }
+  return ok();
+}
+
+size_t mcs_group_kmeans_workspace_bytes(const mcs_dims* dims) {
+  if (check_dims(dims) != MCS_OK || check_kmeans(dims) != MCS_OK) return 0;
+  return km_ws(dims).total;
+}
+
+int32_t mcs_group_kmeans(const mcs_dims* dims, const uint16_t* q, int32_t iters, int32_t* perm,
+                         int32_t* labels, void* workspace, size_t workspace_bytes, void* stream) {
+  MCS_TRY(check_dims(dims));
+  MCS_TRY(check_kmeans(dims));
+  MCS_TRY(check_ptr(q, "q"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  MCS_TRY(check_ptr(labels, "labels", true));
+  if (iters < 0 || iters > 1000)
+    return fail(MCS_ERR_INVALID_ARG, "iters %d outside 0 .. 1000", iters);
+  const KmWs w = km_ws(dims);
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(MCS_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MCS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int G = dims->n_pad / dims->group_size;
+  int32_t* bufs[2] = {perm, (int32_t*)(ws + w.perm)};
+  int cur = iters % 2;  // the last iteration writes `perm`
+  mcs::PddpParams ip{};
+  ip.perm_cur = bufs[cur];
+  ip.bh = (int64_t)dims->batch * dims->heads;
+  ip.n_pad = dims->n_pad;
+  MCS_TRY(hip_status(mcs::launch_pddp_identity(ip, s), "k-means initial partition"));
+  mcs::KmeansParams p{};
+  p.q = q;
+  p.sq = bhnd_strides(dims);
+  p.labels = labels != nullptr ? labels : (int32_t*)(ws + w.labels);
+  p.cent = (uint16_t*)(ws + w.cent);
+  p.cnorm = (float*)(ws + w.cnorm);
+  p.counts = (int32_t*)(ws + w.counts);
+  p.bh = (int64_t)dims->batch * dims->heads;
+  p.heads = dims->heads;
+  p.n_pad = dims->n_pad;
+  p.groups = G;
+  p.tiles = (dims->n_pad + mcs::KM_TILE - 1) / mcs::KM_TILE;
+  p.label_bits = levels_for(G);
+  for (int it = 0; it < iters; ++it) {
+    p.perm_cur = bufs[cur];
+    p.perm_next = bufs[1 - cur];
+    MCS_TRY(hip_status(mcs::launch_km_centroids(dims->head_dim, dims->group_size, p, s),
+                       "k-means centroids"));
+    MCS_TRY(hip_status(mcs::launch_km_assign(dims->head_dim, p, s), "k-means assignment"));
+    MCS_TRY(hip_status(mcs::launch_km_balance(p, s), "k-means balancing"));
     cur = 1 - cur;
   }
   return ok();

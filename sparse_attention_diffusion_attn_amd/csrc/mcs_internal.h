@@ -106,6 +106,22 @@ struct PddpParams {
   int32_t fix_sign;       // reduce stage 1: apply the sign rule to v (last power step)
 };
 
+// Size-balanced k-means grouping (the comparator of Fast PDDP).
+constexpr int KM_TILE = 1024;     // tokens per tile of the balancing sort
+constexpr int KM_MAX_GROUPS = 8192;
+struct KmeansParams {
+  const uint16_t* q;
+  Strides sq;
+  const int32_t* perm_cur;  // [BH, n_pad] current partition
+  int32_t* perm_next;       // [BH, n_pad] balanced partition of this iteration
+  int32_t* labels;          // [BH, n_pad] nearest centroid of each token
+  uint16_t* cent;           // [BH, G, d] bf16 centroids
+  float* cnorm;             // [BH, G] squared norms of the bf16 centroids
+  int32_t* counts;          // [BH, tiles, G] per-tile label counts, then run starts
+  int64_t bh;
+  int32_t heads, n_pad, groups, tiles, label_bits;
+};
+
 hipError_t launch_attention(int mode, int head_dim, int group_size, const AttnParams& p,
                             hipStream_t s);
 hipError_t launch_scores(int head_dim, int group_size, const ScoreParams& p, hipStream_t s);
@@ -124,5 +140,10 @@ hipError_t launch_pddp_partial(int head_dim, int group_size, int stage, const Pd
 hipError_t launch_pddp_reduce(int head_dim, int group_size, int stage, const PddpParams& p,
                               hipStream_t s);
 hipError_t launch_pddp_split(int group_size, const PddpParams& p, hipStream_t s);
+
+hipError_t launch_km_centroids(int head_dim, int group_size, const KmeansParams& p, hipStream_t s);
+hipError_t launch_km_assign(int head_dim, const KmeansParams& p, hipStream_t s);
+// count, scan and stable scatter: labels -> perm_next
+hipError_t launch_km_balance(const KmeansParams& p, hipStream_t s);
 
 }  // namespace mcs

@@ -11,6 +11,14 @@ only keys scoring at least tau' - eps, and have exactly k distinct members.
 Grouping: level by level, the GPU's partition at depth l-1 is fed to the
 oracle's split; the children must match as sets, except for rows whose oracle
 projection lies within EPS_PDDP * max|p| of the node's split boundary.
+
+Balanced k-means (the PDDP comparator): iteration by iteration, the GPU's
+previous partition is fed to the oracle.  Centroids (fp64 means rounded once
+to bf16) are the same on both sides; a GPU label must be a nearest centroid up
+to the fp32 accumulation margin EPS_KM * (2 sum|x.mu| + ||mu||^2), and equal to
+the oracle's wherever the best centroid beats every other by more than the
+margins; the GPU's new partition must be exactly the oracle's balance of the
+GPU's labels.
 """
 from __future__ import annotations
 
@@ -25,6 +33,10 @@ EPS_PDDP = 1e-9
 # block selections (oracle-analysis variants): block scores are fp64 sums
 # ranked in fp32 on the GPU; ties are resolved within EPS_BLK * max|score|
 EPS_BLK = 1e-5
+# k-means distances: bf16 dot products of d <= 128 terms accumulated in fp32
+# (|error| <= d * 2^-24 * sum|x.mu| ~ 2^-17 of it), then one fma with the fp32
+# ||mu||^2; 2^-14 covers both, with a factor 4 to spare
+EPS_KM = 2.0 ** -14
 
 
 def bf16_to_f64(t) -> np.ndarray:
@@ -117,3 +129,31 @@ def check_split_level(q_head, perm_prev, perm_gpu, C, G, level, power_iters=20):
             assert diff <= band_tok, f"split differs outside the band ({len(diff - band_tok)} rows)"
             swaps += len(diff) // 2
     return swaps
+
+
+def check_kmeans_step(x_head, perm_prev, labels_gpu, perm_gpu, C):
+    """Check one GPU k-means iteration given the GPU's partition before it.
+    Returns the number of tokens whose GPU label differs from the oracle's
+    inside the rounding margin."""
+    from oracle import kmeans as okm
+
+    x = np.asarray(x_head, np.float64)
+    lab = np.asarray(labels_gpu, np.int64)
+    mu = okm.centroids(x, perm_prev, C)
+    dist = okm.distances(x, mu)
+    margin = EPS_KM * (2.0 * (np.abs(x) @ np.abs(mu).T) + (mu * mu).sum(axis=1)[None, :])
+    rows = np.arange(x.shape[0])
+    assert lab.min() >= 0 and lab.max() < mu.shape[0], "label out of range"
+    lo = dist - margin
+    hi = dist + margin
+    # the GPU's choice may not be beaten by any centroid outside the margins
+    assert np.all(lo[rows, lab] <= hi.min(axis=1)), "a GPU label is not a nearest centroid"
+    best = okm.assign(x, mu)
+    hi_best = hi[rows, best]
+    lo_other = lo.copy()
+    lo_other[rows, best] = np.inf
+    unique = hi_best < lo_other.min(axis=1)
+    assert np.array_equal(lab[unique], best[unique]), "an unambiguous label differs"
+    assert np.array_equal(np.asarray(perm_gpu, np.int64), okm.balance(lab, C)), \
+        "partition is not the balance of the labels"
+    return int((lab != best).sum())

@@ -241,3 +241,26 @@ def test_strided_extent_one_strides_ignored_and_alias_rules():
     assert lib.mcs_dense_attn_strided(b, ctypes.byref(lay), P, P, P, 0.1, P, None,
                                       None) == mcs.MCS_ERR_INVALID_ARG
     assert "alias" in err()
+
+
+def test_kmeans_checks():
+    lib = mcs.lib()
+    dm = d()                                  # 2 heads, n_pad 1024, d 128, C 128: 8 groups
+    b = ctypes.byref(dm)
+    G, bh, tiles = 8, 2, 1
+    want = 0
+    for nbytes in (bh * 1024 * 4, bh * 1024 * 4, bh * G * 128 * 2, bh * G * 4, bh * tiles * G * 4):
+        want = (want + nbytes + 255) // 256 * 256
+    need = lib.mcs_group_kmeans_workspace_bytes(b)
+    assert need == want
+    big = mcs.make_dims(1, 1, 8193 * 64, 8193 * 64, 64, 64)
+    assert lib.mcs_group_kmeans_workspace_bytes(ctypes.byref(big)) == 0
+    assert lib.mcs_group_kmeans(ctypes.byref(big), P, 3, P, None, P, 1 << 30, None) == mcs.MCS_ERR_UNSUPPORTED
+    assert "8192" in err()
+    assert lib.mcs_group_kmeans(b, P, -1, P, None, P, need, None) == mcs.MCS_ERR_INVALID_ARG
+    assert "iters" in err()
+    assert lib.mcs_group_kmeans(b, P, 1001, P, None, P, need, None) == mcs.MCS_ERR_INVALID_ARG
+    assert lib.mcs_group_kmeans(b, P, 3, None, None, P, need, None) == mcs.MCS_ERR_INVALID_ARG
+    assert lib.mcs_group_kmeans(b, P, 3, P, MIS, P, need, None) == mcs.MCS_ERR_INVALID_ARG
+    assert lib.mcs_group_kmeans(b, P, 3, P, None, P, need - 1, None) == mcs.MCS_ERR_WORKSPACE
+    assert lib.mcs_group_kmeans(b, P, 3, P, None, P + 16, need, None) == mcs.MCS_ERR_WORKSPACE
