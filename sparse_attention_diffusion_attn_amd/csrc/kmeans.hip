@@ -32,28 +32,45 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return f32_to_bf16(__uint_as_float(u));
 }
 
+// One workgroup per (head, group): thread (dg, rg) reads 16 bytes (8 dims) of
+// rows rg, rg + RG, ... of the group, all loads in flight at once.
 template <int D, int C>
 __global__ __launch_bounds__(256) void km_centroid_kernel(KmeansParams p) {
-  constexpr int NT = 256, PARTS = NT / D;
-  __shared__ double part[NT];
-  __shared__ double sq[NT];
+  constexpr int DG = D / 8, RG = 256 / DG, RPT = C / RG;
+  __shared__ double part[RG][D];
+  __shared__ double sq[D];
   const int G = p.groups;
   const int64_t bh = blockIdx.x / G;
   const int g = (int)(blockIdx.x - bh * G);
   const uint16_t* Q = p.q + head_offset(p.sq, bh, p.heads);
   const int32_t* mem = p.perm_cur + bh * p.n_pad + (int64_t)g * C;
-  const int tid = threadIdx.x, d = tid % D, pt = tid / D;
-  double s = 0.0;
-  for (int r = pt; r < C; r += PARTS) {
-    const int row = mem[r];
-    if ((unsigned)row < (unsigned)p.n_pad) s += (double)bf16_to_f32(Q[(int64_t)row * p.sq.n + d]);
+  const int tid = threadIdx.x, dg = tid % DG, rg = tid / DG;
+  uint4 xr[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int row = mem[rg + k * RG];
+    xr[k] = make_uint4(0, 0, 0, 0);
+    if ((unsigned)row < (unsigned)p.n_pad) xr[k] = *(const uint4*)(Q + (int64_t)row * p.sq.n + 8 * dg);
   }
-  part[tid] = s;
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const uint32_t w4[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += (double)__uint_as_float(w4[e] << 16);
+      acc[2 * e + 1] += (double)__uint_as_float(w4[e] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][8 * dg + e] = acc[e];
   __syncthreads();
   if (tid < D) {
-    double t = part[tid];
+    double t = part[0][tid];
 #pragma unroll
-    for (int q = 1; q < PARTS; ++q) t += part[q * D + tid];
+    for (int q = 1; q < RG; ++q) t += part[q][tid];
     const uint16_t c = f64_to_bf16(t / (double)C);
     p.cent[(bh * G + g) * D + tid] = c;
     const double cv = (double)bf16_to_f32(c);
@@ -91,19 +108,34 @@ __global__ __launch_bounds__(256) void km_assign_kernel(KmeansParams p) {
 
   const uint16_t* cent = p.cent + bh * G * D;
   const float* cnorm = p.cnorm + bh * G;
+  // the next centroid tile (64 rows x D/8 chunks of 16 bytes) is loaded into
+  // registers while the current one is used
+  constexpr int NL = CT * (D / 8) / 256;
+  uint4 nv[NL];
+  float nn = INFINITY;
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      const int r = i / (D / 8), ch = i % (D / 8);
+      nv[k] = make_uint4(0, 0, 0, 0);
+      if (c0 + r < G) nv[k] = *(const uint4*)(cent + (int64_t)(c0 + r) * D + 8 * ch);
+    }
+    if (threadIdx.x < CT) nn = (c0 + (int)threadIdx.x < G) ? cnorm[c0 + threadIdx.x] : INFINITY;
+  };
   float best = INFINITY;
   int bidx = 0;
+  load(0);
   for (int c0 = 0; c0 < G; c0 += CT) {
     __syncthreads();
-    // 64 rows x D/8 chunks of 16 bytes
-    for (int i = threadIdx.x; i < CT * (D / 8); i += 256) {
-      const int r = i / (D / 8), ch = i % (D / 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c0 + r < G) v = *(const uint4*)(cent + (int64_t)(c0 + r) * D + 8 * ch);
-      *(uint4*)(cl + r * PITCH + 16 * ch) = v;
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      *(uint4*)(cl + (i / (D / 8)) * PITCH + 16 * (i % (D / 8))) = nv[k];
     }
-    if (threadIdx.x < CT) cn[threadIdx.x] = (c0 + threadIdx.x < G) ? cnorm[c0 + threadIdx.x] : INFINITY;
+    if (threadIdx.x < CT) cn[threadIdx.x] = nn;
     __syncthreads();
+    if (c0 + CT < G) load(c0 + CT);
     f32x16 s0, s1;
 #pragma unroll
     for (int j = 0; j < 16; ++j) { s0[j] = 0.f; s1[j] = 0.f; }
