@@ -247,6 +247,30 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
         double c = 0.0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) c = __builtin_fma(mu8[e], v8[e], c);
+        if (STAGE == 1) {
+          // one conversion per row: t_r = x_r . v - c over the DG lanes of the
+          // row, then acc += t_r x_r from the same registers (the sums run
+          // over the rows in the same order as a separate second sweep would)
+          double tsum = 0.0;
+#pragma unroll
+          for (int k = 0; k < RPT; ++k) {
+            double x[8];
+            to_f64(xr[k], x);
+            double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              a0 = __builtin_fma(x[e], v8[e], a0);
+              a1 = __builtin_fma(x[e + 1], v8[e + 1], a1);
+            }
+            const double tk = group_sum<DG>((a0 + a1) - c);
+            tsum += tk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(tk, x[e], acc[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(-mu8[e], tsum, acc[e]);
+          store_totals(bh, g, acc);
+        } else {
         // t_r = x_r . v - c summed over the DG lanes of row r
         double t[RPT];
 #pragma unroll
@@ -261,31 +285,11 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
           }
           t[k] = group_sum<DG>((a0 + a1) - c);
         }
-        if (STAGE == 2) {
-          if (dg == 0) {
-            double* pr = p.proj + (size_t)bh * p.n_pad + (size_t)g * C;
+        if (dg == 0) {
+          double* pr = p.proj + (size_t)bh * p.n_pad + (size_t)g * C;
 #pragma unroll
-            for (int k = 0; k < RPT; ++k) pr[rg + k * RG] = t[k];
-          }
-        } else {
-          // w_d = sum_r t_r x_rd - mu_d sum_r t_r over this thread's rows (the
-          // rows are converted again: keeping all of them as doubles would
-          // take 4*RPT more VGPRs than the bf16 copies)
-#pragma unroll
-          for (int k = 0; k < RPT; ++k)
-            asm volatile("" : "+v"(xr[k].x), "+v"(xr[k].y), "+v"(xr[k].z), "+v"(xr[k].w));
-          double tsum = 0.0;
-#pragma unroll
-          for (int k = 0; k < RPT; ++k) {
-            tsum += t[k];
-            double x[8];
-            to_f64(xr[k], x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(t[k], x[e], acc[e]);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(-mu8[e], tsum, acc[e]);
-          store_totals(bh, g, acc);
+          for (int k = 0; k < RPT; ++k) pr[rg + k * RG] = t[k];
+        }
         }
       }
     }

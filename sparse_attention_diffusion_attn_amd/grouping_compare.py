@@ -109,7 +109,7 @@ def compare(cfg, iters_list, reps=3):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--configs", default="480p,wan720p,hunyuan720p,3d")
+    ap.add_argument("--configs", default="480p,wan720p,hunyuan720p_15,3d")
     ap.add_argument("--layout", default="random")
     ap.add_argument("--iters", default="1,5,10,20")
     args = ap.parse_args()
@@ -131,7 +131,8 @@ def main():
             es = f" err {e['no_residual']:.4f}/{e['residual']:.4f}" if e else ""
             print(f"#   k-means {it:3d} iters: {k['ms']:.2f} ms spread {k['spread']:.4f}{es}",
                   file=sys.stderr)
-        print(f"#   k-means per iteration: {r['kmeans_ms_per_iter']:.3f} ms", file=sys.stderr, flush=True)
+        if r["kmeans_ms_per_iter"] is not None:
+            print(f"#   k-means per iteration: {r['kmeans_ms_per_iter']:.3f} ms", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     print(json.dumps({"grouping_compare": rows}))
 
