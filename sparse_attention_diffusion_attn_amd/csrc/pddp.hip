@@ -64,11 +64,13 @@ __global__ void pddp_identity_kernel(int32_t* perm, int n_pad, int64_t total) {
 }
 
 // fp64 value of another lane, moved by a DPP lane pattern (both 32-bit halves).
+// Every pattern used here has a source lane inside the row for every lane,
+// so no "old" value is needed (and none is materialised).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 // Sum over aligned groups of N = 8 or 16 lanes, the same bits in every lane of
