@@ -259,6 +259,27 @@ def main():
     dense_flops = 4.0 * B * H * n_pad * nv * d
     dense_tflops = dense_flops / (td * 1e-3) / 1e12
 
+    # torch's own fused attention at the same shape (valid tokens only), as a
+    # sanity reference for the dense kernel; not a target
+    sdpa_ms = None
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        qs, ks_, vs = q1[:, :, :nv], k1[:, :, :nv], v1[:, :, :nv]
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            torch.nn.functional.scaled_dot_product_attention(qs, ks_, vs, scale=sc)
+            t_sd = []
+            for _ in range(3):
+                flush.sum()
+                a, b = ev(), ev()
+                a.record()
+                torch.nn.functional.scaled_dot_product_attention(qs, ks_, vs, scale=sc)
+                b.record()
+                torch.cuda.synchronize()
+                t_sd.append(a.elapsed_time(b))
+        sdpa_ms = statistics.median(t_sd)
+    except (RuntimeError, ImportError) as e:  # no fused backend for this shape / build
+        print(f"# torch SDPA reference skipped: {e}", file=sys.stderr)
+
     kernel_hash = source_hash("attn.hip", "mcs_common.h")
     traffic = load_traffic(kernel_hash)
     roofline = {"bound": "mfma", "achieved": round(eff_tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -266,6 +287,17 @@ def main():
                 "traffic": traffic, "kernel": "attn_kernel<128,128,SPARSE> (mcs_sparse_attn)",
                 "flops_per_launch": sparse_flops, "avg_launch_ms": round(t_sparse_ms, 4),
                 "kernel_src_hash": kernel_hash}
+    # the HBM side of the same launch: L2-fill bytes per launch (the traffic
+    # counters) over its time, against the 8 TB/s peak; and the rate at which
+    # the kernel consumes gathered K/V rows (4 * k * (d + 1) bytes per group,
+    # K and V rows plus the index), mostly served by L2 / MALL
+    gathered = 4.0 * B * H * (n_pad // C) * k * (d + 1)
+    hbm = {"gathered_bytes_per_launch": gathered,
+           "gathered_GBps": round(gathered / (t_sparse_ms * 1e-3) / 1e9, 1)}
+    if traffic is not None:
+        gbps = traffic / (t_sparse_ms * 1e-3) / 1e9
+        hbm.update({"traffic_GBps": round(gbps, 1), "hbm_peak_GBps": PEAK_HBM_GBS,
+                    "hbm_frac": round(gbps / PEAK_HBM_GBS, 4)})
 
     cpu = None
     if not args.no_cpu:
@@ -298,13 +330,18 @@ def main():
         "dense_ms": round(td, 4),
         "sparse_ms": round(ts, 4),
         "ideal_1_over_s_frac_alternating": round(ideal_frac_alt, 4),
+        "dense_ms_min": round(min(t_d), 4),
+        "sparse_ms_min": round(min(t_s), 4),
         "dense_tflops": round(dense_tflops, 2),
+        "torch_sdpa_ms": None if sdpa_ms is None else round(sdpa_ms, 4),
+        "dense_speedup_vs_torch_sdpa": None if sdpa_ms is None else round(sdpa_ms / td, 3),
         "dense_mfma_frac": round(dense_tflops / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {n: round(statistics.mean(v), 4) for n, v in stage_ms.items()},
         # extra anchor work over a dense step, spread over the anchor's steps,
         # in units of the dense step (density-equivalent overhead)
         "anchor_overhead_ds": round((anchor_ms - td) / (cfg.n_reuse + 1) / td, 4),
         "roofline": roofline,
+        "sparse_hbm": hbm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
