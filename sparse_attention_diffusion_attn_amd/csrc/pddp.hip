@@ -135,7 +135,6 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
 
   const int G = p.groups;
   const int64_t nblk = p.bh * (int64_t)G;
-  const int64_t P = gridDim.x;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -146,29 +145,43 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   const __amdgpu_buffer_rsrc_t vrs =
       make_rsrc(p.vec, (uint32_t)min<int64_t>(nblk * D * 8, 0xffffffffll));
 
-  // perm indices of this thread's rows in block b
-  auto load_idx = [&](int64_t b, int (&ix)[RPT]) {
-    const int64_t bh = b / G;
-    const int g = (int)(b - bh * G);
-    const int32_t* pc = p.perm_cur + bh * p.n_pad + (int64_t)g * C;
+  // Block b = bh * G + g.  A workgroup takes blocks b, b + P, b + 2P, ... (P =
+  // grid size); the (head, group) pairs of the next blocks are stepped with a
+  // carry instead of divided out again (the divisions were most of the
+  // per-block scalar work).
+  struct Pos {
+    int bh, g;
+  };
+  const int P = gridDim.x;
+  const int dbh = P / G, dg_step = P - dbh * G;
+  auto step = [&](Pos q) {
+    q.g += dg_step;
+    q.bh += dbh;
+    if (q.g >= G) {
+      q.g -= G;
+      ++q.bh;
+    }
+    return q;
+  };
+  const int nbh = (int)p.bh;
+
+  // perm indices of this thread's rows in block q
+  auto load_idx = [&](Pos q, int (&ix)[RPT]) {
+    const int32_t* pc = p.perm_cur + (int64_t)q.bh * p.n_pad + (int64_t)q.g * C;
 #pragma unroll
     for (int k = 0; k < RPT; ++k) ix[k] = pc[rg + k * RG];
   };
   // this thread's 8 bf16 of each of its rows (16 bytes each)
-  auto load_rows = [&](int64_t b, const int (&ix)[RPT], uint4 (&xr)[RPT]) {
-    const int64_t bh = b / G;
-    const uint16_t* Qb = p.q + head_offset(p.sq, bh, p.heads);
+  auto load_rows = [&](Pos q, const int (&ix)[RPT], uint4 (&xr)[RPT]) {
+    const uint16_t* Qb = p.q + head_offset(p.sq, q.bh, p.heads);
 #pragma unroll
     for (int k = 0; k < RPT; ++k) xr[k] = *(const uint4*)(Qb + (int64_t)ix[k] * p.sq.n + 8 * dg);
   };
-  // mu and v of block b's node into LDS half `buf` (one 16-byte copy per lane
-  // of waves 0 and 1; for D = 64 the upper half of the copy is not used)
-  auto load_muv = [&](int64_t b, int buf) {
+  // mu and v of the node starting at group s into LDS half `buf` (one 16-byte
+  // copy per lane of waves 0 and 1; for D = 64 the upper half is not used)
+  auto load_muv = [&](Pos q, int s, int buf) {
     if (STAGE == 0 || w > 1) return;
-    const int64_t bh = b / G;
-    int s, m;
-    node_of(G, p.level, (int)(b - bh * G), s, m);
-    const uint32_t off = (uint32_t)(((bh * G + s) * D) * 8) + 16u * (uint32_t)lane;
+    const uint32_t off = (uint32_t)((((int64_t)q.bh * G + s) * D) * 8) + 16u * (uint32_t)lane;
     if (w == 0) gather16_buf(murs, &muv[buf][0][0], off, 0);
     else gather16_buf(vrs, &muv[buf][1][0], off, 0);
   };
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   };
   // per-dimension block totals: acc[e] (dimension 8dg+e, this thread's rows)
   // summed over the wavefront's row groups, then over the wavefronts in order
-  auto store_totals = [&](int64_t bh, int g, double (&acc)[8]) {
+  auto store_totals = [&](int bh, int g, double (&acc)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       double x = acc[e];
@@ -204,30 +217,33 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
     }
   };
 
-  int64_t b = blockIdx.x;
-  if (b >= nblk) return;
+  if ((int64_t)blockIdx.x >= nblk) return;
+  Pos cur = {(int)(blockIdx.x / G), (int)(blockIdx.x % G)};
+  Pos nxt = step(cur);
+  Pos nxt2 = step(nxt);
+  int s, m, s_n = 0, m_n = 0;
+  node_of(G, p.level, cur.g, s, m);
   int idx_n[RPT];
   uint4 xr[RPT], xr_n[RPT];
-  load_idx(b, idx_n);
+  load_idx(cur, idx_n);
   wait_vm0();
-  load_rows(b, idx_n, xr);
-  load_muv(b, 0);
-  if (b + P < nblk) load_idx(b + P, idx_n);
+  load_rows(cur, idx_n, xr);
+  load_muv(cur, s, 0);
+  if (nxt.bh < nbh) load_idx(nxt, idx_n);
 
-  for (int it = 0; b < nblk; ++it, b += P) {
+  for (int it = 0; cur.bh < nbh; ++it) {
     wait_vm0();
     __syncthreads();
     const int buf = it & 1;
-    // prefetch block b + P (rows, mu / v) and the indices of block b + 2P
-    if (b + P < nblk) {
-      load_rows(b + P, idx_n, xr_n);
-      load_muv(b + P, buf ^ 1);
-      if (b + 2 * P < nblk) load_idx(b + 2 * P, idx_n);
+    // prefetch the next block (rows, mu / v) and the indices of the one after
+    if (nxt.bh < nbh) {
+      load_rows(nxt, idx_n, xr_n);
+      node_of(G, p.level, nxt.g, s_n, m_n);
+      load_muv(nxt, s_n, buf ^ 1);
+      if (nxt2.bh < nbh) load_idx(nxt2, idx_n);
     }
-    const int64_t bh = b / G;
-    const int g = (int)(b - bh * G);
-    int s, m;
-    node_of(G, p.level, g, s, m);
+    const int bh = cur.bh;
+    const int g = cur.g;
     if (m >= 2) {
       double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (STAGE == 0) {
@@ -297,6 +313,11 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
     }
 #pragma unroll
     for (int k = 0; k < RPT; ++k) xr[k] = xr_n[k];
+    cur = nxt;
+    nxt = nxt2;
+    nxt2 = step(nxt2);
+    s = s_n;
+    m = m_n;
   }
 }
 
