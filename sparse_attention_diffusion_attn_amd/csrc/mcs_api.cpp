@@ -189,13 +189,36 @@ int32_t resolve_layout(const mcs_dims* d, const mcs_layout* l, Lay* out) {
 }
 
 // ---- workspace layouts ----
+// Depths whose largest node holds at least gram_min(d) groups run the power
+// iteration on the node's covariance (Gram path); the others on the rows.
+// With d = 128 the covariance takes 128 KiB of LDS per node, one node per CU,
+// which loses to the row passes once nodes are small (measured: 8 groups is
+// the break-even); with d = 64 (32 KiB) it wins down to 2-group nodes.
+int gram_min(int head_dim) { return head_dim == 64 ? 2 : 8; }
+
+int gram_largest_node(int groups, int level) {  // ceil(G / 2^level)
+  return (int)(((int64_t)groups + ((int64_t)1 << level) - 1) >> level);
+}
+bool gram_level(int groups, int level, int head_dim) {
+  return gram_largest_node(groups, level) >= gram_min(head_dim);
+}
+int gram_chunks(int groups, int level) {
+  return (gram_largest_node(groups, level) + mcs::GRAM_CH - 1) / mcs::GRAM_CH;
+}
+
 struct GroupWs {
-  size_t partial, mu, vec, proj, perm, total;
+  size_t partial, mu, vec, proj, perm, gram, total;
 };
 
 GroupWs group_ws(const mcs_dims* d) {
   const size_t bh = (size_t)d->batch * d->heads;
   const size_t G = (size_t)(d->n_pad / d->group_size);
+  const size_t dt = (size_t)d->head_dim / 16;
+  const size_t tile_doubles = dt * (dt + 1) / 2 * 256;
+  size_t gram = 0;  // chunk partials of the largest Gram depth
+  for (int l = 0; l < levels_for((int)G); ++l)
+    if (gram_level((int)G, l, d->head_dim))
+      gram = std::max(gram, ((size_t)1 << l) * (size_t)gram_chunks((int)G, l) * tile_doubles);
   GroupWs w;
   size_t o = 0;
   w.partial = o; o = align256(o + bh * G * d->head_dim * sizeof(double));
@@ -203,6 +226,7 @@ GroupWs group_ws(const mcs_dims* d) {
   w.vec = o;     o = align256(o + bh * G * d->head_dim * sizeof(double));
   w.proj = o;    o = align256(o + bh * (size_t)d->n_pad * sizeof(double));
   w.perm = o;    o = align256(o + bh * (size_t)d->n_pad * sizeof(int32_t));
+  w.gram = o;    o = align256(o + bh * gram * sizeof(double));
   w.total = o;
   return w;
 }
@@ -373,6 +397,8 @@ int32_t mcs_group_strided(const mcs_dims* dims, const mcs_layout* layout, const 
   p.mu = (double*)(ws + w.mu);
   p.vec = (double*)(ws + w.vec);
   p.proj = (double*)(ws + w.proj);
+  p.gram = (double*)(ws + w.gram);
+  p.power_iters = power_iters;
   p.sq = lay.q;
   p.bh = (int64_t)dims->batch * dims->heads;
   p.heads = dims->heads;
@@ -388,10 +414,16 @@ int32_t mcs_group_strided(const mcs_dims* dims, const mcs_layout* layout, const 
     p.perm_next = bufs[1 - cur];
     MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 0, p, s), "pddp mean"));
     MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 0, p, s), "pddp mean reduce"));
-    for (int it = 0; it < power_iters; ++it) {
-      p.fix_sign = (it == power_iters - 1) ? 1 : 0;
-      MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 1, p, s), "pddp power step"));
-      MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 1, p, s), "pddp power reduce"));
+    if (power_iters > 0 && gram_level(G, lv, d)) {
+      p.nch = gram_chunks(G, lv);
+      MCS_TRY(hip_status(mcs::launch_pddp_gram(d, c, p, s), "pddp covariance"));
+      MCS_TRY(hip_status(mcs::launch_pddp_gram_power(d, c, p, s), "pddp covariance power"));
+    } else {
+      for (int it = 0; it < power_iters; ++it) {
+        p.fix_sign = (it == power_iters - 1) ? 1 : 0;
+        MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 1, p, s), "pddp power step"));
+        MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 1, p, s), "pddp power reduce"));
+      }
     }
     p.fix_sign = 0;
     MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 2, p, s), "pddp projection"));

@@ -104,7 +104,13 @@ struct PddpParams {
   int32_t heads;
   int32_t n_pad, groups, level;
   int32_t fix_sign;       // reduce stage 1: apply the sign rule to v (last power step)
+  double* gram;           // Gram path: chunk partials [BH, 2^level, nch, tiles, 256]
+  int32_t nch;            // Gram path: chunks per node slot at this depth
+  int32_t power_iters;    // Gram path: power iterations
 };
+
+// Blocks (of C rows) per work item of the Gram path.
+constexpr int GRAM_CH = 8;
 
 // Size-balanced k-means grouping (the comparator of Fast PDDP).
 constexpr int KM_TILE = 1024;     // tokens per tile of the balancing sort
@@ -140,6 +146,11 @@ hipError_t launch_pddp_partial(int head_dim, int group_size, int stage, const Pd
 hipError_t launch_pddp_reduce(int head_dim, int group_size, int stage, const PddpParams& p,
                               hipStream_t s);
 hipError_t launch_pddp_split(int group_size, const PddpParams& p, hipStream_t s);
+// Gram path of a depth: chunk partials of X^T X (launch_pddp_gram), then
+// (launch_pddp_gram_power) their sum per node and, per node, the centred
+// matrix, the power iterations and the sign rule (writes v)
+hipError_t launch_pddp_gram(int head_dim, int group_size, const PddpParams& p, hipStream_t s);
+hipError_t launch_pddp_gram_power(int head_dim, int group_size, const PddpParams& p, hipStream_t s);
 
 hipError_t launch_km_centroids(int head_dim, int group_size, const KmeansParams& p, hipStream_t s);
 hipError_t launch_km_assign(int head_dim, const KmeansParams& p, hipStream_t s);

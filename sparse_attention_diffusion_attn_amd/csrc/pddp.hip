@@ -12,6 +12,8 @@
 // reduction has a fixed order and results are bitwise reproducible.  The split
 // is an exact radix select on the fp64 projections (64-bit order-preserving
 // keys, ties broken by position = token index) followed by a stable partition.
+#include <utility>
+
 #include "mcs_common.h"
 #include "mcs_internal.h"
 
@@ -550,6 +552,270 @@ __global__ __launch_bounds__(512) void pddp_split_kernel(PddpParams p) {
   }
 }
 
+// ---- Gram path for the upper depths ----
+// At a depth whose nodes hold many groups, the power iteration runs on the
+// node's centred covariance instead of on its rows:
+//   Sigma = X^T X - n mu mu^T   (fp64, d x d, n = m*C rows, padding rows included)
+// which is the same operator v -> sum_r ((x_r - mu) . v)(x_r - mu), formed with
+// one pass over the rows on the fp64 matrix cores; the 20 iterations then cost
+// d^2 work per node instead of a pass over its rows each.
+//
+// pddp_gram_kernel: one workgroup per (head, node slot, chunk of GRAM_CH
+// blocks); X^T X of the chunk's rows with v_mfma_f64_16x16x4_f64, only the
+// upper-triangular 16x16 tiles (I <= J), written as a partial per chunk.
+// pddp_gram_power_kernel: one workgroup per node; sums the node's chunk
+// partials in chunk order, centres, runs the power iterations (v0 = 1/sqrt(d),
+// v kept when |Sigma v| = 0) and applies the sign rule, as the row path does.
+
+template <int DT>
+__host__ __device__ constexpr int gram_tile_i(int t) {
+  int i = 0, len = DT;
+  while (t >= len) {
+    t -= len;
+    ++i;
+    --len;
+  }
+  return i;
+}
+template <int DT>
+__host__ __device__ constexpr int gram_tile_j(int t) {
+  int i = 0, len = DT;
+  while (t >= len) {
+    t -= len;
+    ++i;
+    --len;
+  }
+  return i + t;
+}
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// tile t = W + 4K of the wave's share: acc += X[:, 16I..] (A) x X[:, 16J..] (B)
+template <int DT, int W, int K>
+__device__ __forceinline__ void gram_mfma(const double (&xv)[DT], f64x4& acc) {
+  constexpr int t = W + 4 * K;
+  if constexpr (t < DT * (DT + 1) / 2) {
+    constexpr int I = gram_tile_i<DT>(t);
+    constexpr int J = gram_tile_j<DT>(t);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[I], xv[J], acc, 0, 0, 0);
+  }
+}
+template <int DT, int W, int... K>
+__device__ __forceinline__ void gram_mfmas(const double (&xv)[DT], f64x4 (&acc)[sizeof...(K)],
+                                           std::integer_sequence<int, K...>) {
+  (gram_mfma<DT, W, K>(xv, acc[K]), ...);
+}
+// lane l holds D[i][j] of tile t for j = l % 16, i = l / 16 + 4r (r = 0..3);
+// partial tile t is stored row-major (16 x 16)
+template <int DT, int W, int K>
+__device__ __forceinline__ void gram_store(double* dst, const f64x4& acc, int lane) {
+  constexpr int t = W + 4 * K;
+  if constexpr (t < DT * (DT + 1) / 2) {
+    double* tile = dst + t * 256;
+    static_assert(gram_tile_i<DT>(t) <= gram_tile_j<DT>(t), "upper tile");
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tile[(lane / 16 + 4 * r) * 16 + (lane & 15)] = acc[r];
+  }
+}
+template <int DT, int W, int... K>
+__device__ __forceinline__ void gram_stores(double* dst, const f64x4 (&acc)[sizeof...(K)], int lane,
+                                            std::integer_sequence<int, K...>) {
+  (gram_store<DT, W, K>(dst, acc[K], lane), ...);
+}
+
+template <int D, int C, int W>
+__device__ __forceinline__ void gram_body(const PddpParams& p, char (*rows)[64 * (2 * D + 32)],
+                                          const int32_t* pc, const uint16_t* Qb, int nrows,
+                                          double* dst) {
+  constexpr int DT = D / 16, NT = DT * (DT + 1) / 2, TPW = (NT + 3) / 4;
+  constexpr int SUB = 64;                 // rows staged in LDS at a time
+  constexpr int PITCH = 2 * D + 32;       // bytes per staged row (rows 4 apart hit other banks)
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int LPT = SUB * CPR / 256;    // 16-byte loads per thread per stage
+  const int tid = threadIdx.x, lane = tid & 63;
+  f64x4 acc[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) acc[k] = (f64x4){0.0, 0.0, 0.0, 0.0};
+  uint4 nx[LPT];
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) {
+    const int idx = tid + 256 * q;
+    const int row = pc[idx / CPR];
+    nx[q] = *(const uint4*)(Qb + (int64_t)row * p.sq.n + 8 * (idx % CPR));
+  }
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) {
+    const int idx = tid + 256 * q;
+    *(uint4*)(rows[0] + (idx / CPR) * PITCH + 16 * (idx % CPR)) = nx[q];
+  }
+  __syncthreads();
+  for (int r0 = 0, it = 0; r0 < nrows; r0 += SUB, ++it) {
+    const int buf = it & 1;
+    // the next stage's rows (the last stage loads itself again: the unused
+    // copy goes to the buffer no wave reads any more)
+    const int rn = (r0 + SUB < nrows) ? r0 + SUB : r0;
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) {
+      const int idx = tid + 256 * q;
+      const int row = pc[rn + idx / CPR];
+      nx[q] = *(const uint4*)(Qb + (int64_t)row * p.sq.n + 8 * (idx % CPR));
+    }
+    const char* rb = rows[buf];
+#pragma unroll 4
+    for (int st = 0; st < SUB / 4; ++st) {
+      // lane l: row 4*st + l/16 of the stage, dimension 16*blk + l%16
+      const uint16_t* xr = (const uint16_t*)(rb + (4 * st + lane / 16) * PITCH) + (lane & 15);
+      double xv[DT];
+#pragma unroll
+      for (int blk = 0; blk < DT; ++blk) xv[blk] = (double)bf16_to_f32(xr[16 * blk]);
+      gram_mfmas<DT, W>(xv, acc, std::make_integer_sequence<int, TPW>{});
+    }
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) {
+      const int idx = tid + 256 * q;
+      *(uint4*)(rows[buf ^ 1] + (idx / CPR) * PITCH + 16 * (idx % CPR)) = nx[q];
+    }
+    __syncthreads();
+  }
+  gram_stores<DT, W>(dst, acc, lane, std::make_integer_sequence<int, TPW>{});
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void pddp_gram_kernel(
+    PddpParams p) {
+  constexpr int DT = D / 16, NT = DT * (DT + 1) / 2;
+  __shared__ __attribute__((aligned(16))) char rows[2][64 * (2 * D + 32)];
+  const int G = p.groups;
+  const int slots = 1 << p.level;
+  const int per_bh = slots * p.nch;
+  const int bh = blockIdx.x / per_bh;
+  const int rem = blockIdx.x - bh * per_bh;
+  const int slot = rem / p.nch, j = rem - slot * p.nch;
+  int s, m;
+  if (!node_of_slot(G, p.level, slot, s, m) || m < 2) return;
+  const int b0 = j * GRAM_CH;
+  if (b0 >= m) return;
+  const int nrows = (min(b0 + GRAM_CH, m) - b0) * C;
+  const int32_t* pc = p.perm_cur + (int64_t)bh * p.n_pad + (int64_t)(s + b0) * C;
+  const uint16_t* Qb = p.q + head_offset(p.sq, bh, p.heads);
+  double* dst = p.gram + ((int64_t)(bh * slots + slot) * p.nch + j) * (NT * 256);
+  switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: gram_body<D, C, 0>(p, rows, pc, Qb, nrows, dst); break;
+    case 1: gram_body<D, C, 1>(p, rows, pc, Qb, nrows, dst); break;
+    case 2: gram_body<D, C, 2>(p, rows, pc, Qb, nrows, dst); break;
+    default: gram_body<D, C, 3>(p, rows, pc, Qb, nrows, dst); break;
+  }
+}
+
+// Sum of a node's chunk partials, in chunk order, written over chunk 0 (one
+// workgroup per (head, node slot, tile); each thread owns one tile entry, so
+// reading every chunk's value and then writing chunk 0's is safe in place).
+template <int D>
+__global__ __launch_bounds__(256) void pddp_gram_sum_kernel(PddpParams p) {
+  constexpr int DT = D / 16, NT = DT * (DT + 1) / 2;
+  const int G = p.groups;
+  const int slots = 1 << p.level;
+  const int per_bh = slots * NT;
+  const int bh = blockIdx.x / per_bh;
+  const int rem = blockIdx.x - bh * per_bh;
+  const int slot = rem / NT, t = rem - slot * NT;
+  int s, m;
+  if (!node_of_slot(G, p.level, slot, s, m) || m < 2) return;
+  const int nck = (m + GRAM_CH - 1) / GRAM_CH;
+  if (nck < 2) return;
+  double* src = p.gram + (int64_t)(bh * slots + slot) * p.nch * (NT * 256) + t * 256 + threadIdx.x;
+  double a = 0.0;
+  int k = 0;
+  for (; k + 8 <= nck; k += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(k + u) * (NT * 256)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += v[u];
+  }
+  for (; k < nck; ++k) a += src[(int64_t)k * (NT * 256)];
+  src[0] = a;
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
+  constexpr int DT = D / 16, NT = DT * (DT + 1) / 2;
+  constexpr int NTH = 256;
+  __shared__ double sig[D * D];
+  __shared__ double vec[D];
+  __shared__ double red[NTH];
+  __shared__ double vmag[D];
+  __shared__ int vidx[D];
+  const int G = p.groups;
+  const int slots = 1 << p.level;
+  const int bh = blockIdx.x / slots;
+  const int slot = blockIdx.x - bh * slots;
+  int s, m;
+  if (!node_of_slot(G, p.level, slot, s, m) || m < 2) return;
+  const int tid = threadIdx.x;
+  // X^T X of the node (the chunk sums are already in chunk 0), centred and
+  // mirrored to a full matrix
+  const double* src = p.gram + (int64_t)(bh * slots + slot) * p.nch * (NT * 256);
+  double* mu = p.mu + ((size_t)bh * G + s) * D;
+  double* vv = p.vec + ((size_t)bh * G + s) * D;
+  const double n = (double)(m * C);
+  for (int e = tid; e < NT * 256; e += NTH) {
+    const double a = src[e];
+    const int t = e >> 8, li = (e >> 4) & 15, lj = e & 15;
+    int ti = 0, len = DT, tt = t;
+    while (tt >= len) {
+      tt -= len;
+      ++ti;
+      --len;
+    }
+    const int i = 16 * ti + li, jj = 16 * (ti + tt) + lj;
+    const double c = a - n * mu[i] * mu[jj];
+    sig[i * D + jj] = c;
+    sig[jj * D + i] = c;
+  }
+  if (tid < D) vec[tid] = 1.0 / sqrt((double)D);
+  __syncthreads();
+  for (int it = 0; it < p.power_iters; ++it) {
+    double w = 0.0;
+    if (tid < D) {
+      const double* row = sig + tid * D;
+      for (int jj = 0; jj < D; ++jj) w = __builtin_fma(row[jj], vec[jj], w);
+    }
+    red[tid] = (tid < D) ? w * w : 0.0;
+    __syncthreads();
+    for (int o = NTH / 2; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    const double nrm2 = red[0];
+    __syncthreads();
+    if (tid < D && nrm2 > 0.0) vec[tid] = w / sqrt(nrm2);
+    __syncthreads();
+  }
+  // sign rule: the component of largest magnitude (first on ties) positive
+  double nv = (tid < D) ? vec[tid] : 0.0;
+  if (tid < D) {
+    vmag[tid] = fabs(nv);
+    vidx[tid] = tid;
+  }
+  __syncthreads();
+  for (int o = D / 2; o > 0; o >>= 1) {
+    if (tid < o) {
+      const double a = vmag[tid], b = vmag[tid + o];
+      const int ia = vidx[tid], ib = vidx[tid + o];
+      if (b > a || (b == a && ib < ia)) {
+        vmag[tid] = b;
+        vidx[tid] = ib;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == vidx[0]) red[0] = nv;
+  __syncthreads();
+  if (red[0] < 0.0) nv = -nv;
+  if (tid < D) vv[tid] = nv;
+}
+
 hipError_t launch_pddp_identity(const PddpParams& p, hipStream_t s) {
   const int64_t total = p.bh * (int64_t)p.n_pad;
   const unsigned blocks = (unsigned)((total + 255) / 256);
@@ -627,6 +893,33 @@ hipError_t launch_pddp_reduce(int d, int c, int stage, const PddpParams& p, hipS
   if (d == 64 && c == 128) return reduce_t<64, 128>(stage, p, s);
   if (d == 64 && c == 64) return reduce_t<64, 64>(stage, p, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_pddp_gram(int d, int c, const PddpParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)(p.bh * ((int64_t)1 << p.level) * p.nch));
+  if (d == 128 && c == 128) hipLaunchKernelGGL((pddp_gram_kernel<128, 128>), grid, dim3(256), 0, s, p);
+  else if (d == 128 && c == 64) hipLaunchKernelGGL((pddp_gram_kernel<128, 64>), grid, dim3(256), 0, s, p);
+  else if (d == 64 && c == 128) hipLaunchKernelGGL((pddp_gram_kernel<64, 128>), grid, dim3(256), 0, s, p);
+  else if (d == 64 && c == 64) hipLaunchKernelGGL((pddp_gram_kernel<64, 64>), grid, dim3(256), 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_pddp_gram_power(int d, int c, const PddpParams& p, hipStream_t s) {
+  const int nt = (d / 16) * (d / 16 + 1) / 2;
+  const dim3 sgrid((unsigned)(p.bh * ((int64_t)1 << p.level) * nt));
+  if (d == 128) hipLaunchKernelGGL((pddp_gram_sum_kernel<128>), sgrid, dim3(256), 0, s, p);
+  else if (d == 64) hipLaunchKernelGGL((pddp_gram_sum_kernel<64>), sgrid, dim3(256), 0, s, p);
+  else return hipErrorInvalidValue;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(p.bh * ((int64_t)1 << p.level)));
+  if (d == 128 && c == 128) hipLaunchKernelGGL((pddp_gram_power_kernel<128, 128>), grid, dim3(256), 0, s, p);
+  else if (d == 128 && c == 64) hipLaunchKernelGGL((pddp_gram_power_kernel<128, 64>), grid, dim3(256), 0, s, p);
+  else if (d == 64 && c == 128) hipLaunchKernelGGL((pddp_gram_power_kernel<64, 128>), grid, dim3(256), 0, s, p);
+  else if (d == 64 && c == 64) hipLaunchKernelGGL((pddp_gram_power_kernel<64, 64>), grid, dim3(256), 0, s, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_pddp_split(int c, const PddpParams& p, hipStream_t s) {
