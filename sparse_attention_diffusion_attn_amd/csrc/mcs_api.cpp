@@ -192,9 +192,9 @@ int32_t resolve_layout(const mcs_dims* d, const mcs_layout* l, Lay* out) {
 // Depths whose largest node holds at least gram_min(d) groups run the power
 // iteration on the node's covariance (Gram path); the others on the rows.
 // With d = 128 the covariance takes 128 KiB of LDS per node, one node per CU,
-// which loses to the row passes once nodes are small (measured: 8 groups is
-// the break-even); with d = 64 (32 KiB) it wins down to 2-group nodes.
-int gram_min(int head_dim) { return head_dim == 64 ? 2 : 8; }
+// which loses to the row passes once nodes are small (measured: best from 4
+// groups up); with d = 64 (32 KiB) it wins down to 2-group nodes.
+int gram_min(int head_dim) { return head_dim == 64 ? 2 : 4; }
 
 int gram_largest_node(int groups, int level) {  // ceil(G / 2^level)
   return (int)(((int64_t)groups + ((int64_t)1 << level) - 1) >> level);

@@ -776,10 +776,12 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   if (tid < D) vec[tid] = 1.0 / sqrt((double)D);
   __syncthreads();
   for (int it = 0; it < p.power_iters; ++it) {
+    // w_i = sum_j Sigma_ij v_j, read down column i (Sigma is stored symmetric,
+    // so the values and their order are those of row i, and consecutive
+    // lanes read consecutive words)
     double w = 0.0;
     if (tid < D) {
-      const double* row = sig + tid * D;
-      for (int jj = 0; jj < D; ++jj) w = __builtin_fma(row[jj], vec[jj], w);
+      for (int jj = 0; jj < D; ++jj) w = __builtin_fma(sig[jj * D + tid], vec[jj], w);
     }
     red[tid] = (tid < D) ? w * w : 0.0;
     __syncthreads();

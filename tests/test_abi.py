@@ -39,9 +39,10 @@ def test_workspace_sizes():
     G, bh, D = 8, 2, 128
     want = 0
     # partials, mu, v, projections, second perm, then the covariance-path
-    # chunk partials of its largest depth (here the root: 1 node, 1 chunk of
-    # 8 blocks, 36 upper 16x16 fp64 tiles)
-    for nbytes in (bh * G * D * 8,) * 3 + (bh * 1024 * 8, bh * 1024 * 4, bh * 36 * 256 * 8):
+    # chunk partials of its largest depth (depths with nodes of >= 4 groups
+    # for d = 128: depth 1 has 2 node slots of 1 chunk each, 36 upper 16x16
+    # fp64 tiles per chunk)
+    for nbytes in (bh * G * D * 8,) * 3 + (bh * 1024 * 8, bh * 1024 * 4, bh * 2 * 36 * 256 * 8):
         want = (want + nbytes + 255) // 256 * 256
     assert lib.mcs_group_workspace_bytes(ctypes.byref(dm)) == want
     per_head = (G * 1000 * 4 + 255) // 256 * 256 + (G * 1024 * 4 + 255) // 256 * 256
