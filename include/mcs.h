@@ -101,7 +101,9 @@ const char* mcs_last_error(void);
  * index on ties) and its members ordered by (projection, token index); the
  * first floor(m/2)*C go to the left child, the rest to the right.  All nodes of
  * one depth, across all heads, are processed by the same launches and only the
- * index array moves between depths.  Arithmetic is fp64 on the bf16 inputs.
+ * index array moves between depths.  Arithmetic is fp64 on the bf16 inputs; at
+ * depths with large nodes the iteration runs on the node's centred covariance
+ * (X^T X - n mu mu^T, formed once), the same operator as on the rows.
  *   q          : bf16 [B,H,n_pad,d], the anchor step's queries (padding rows 0)
  *   power_iters: 0 .. 1000 (20 in the method's configurations)
  *   max_levels : -1 = all ceil(log2(n_pad/C)) depths; 0..L = stop after that

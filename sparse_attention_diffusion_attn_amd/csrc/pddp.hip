@@ -9,9 +9,12 @@
 // 1-group blocks of perm are natural work units: each per-row pass (mean, power
 // iteration step, projection) runs one workgroup per block and writes a fixed
 // fp64 partial; a per-node kernel sums the partials in block order, so every
-// reduction has a fixed order and results are bitwise reproducible.  The split
-// is an exact radix select on the fp64 projections (64-bit order-preserving
-// keys, ties broken by position = token index) followed by a stable partition.
+// reduction has a fixed order and results are bitwise reproducible.  At the
+// upper depths (large nodes) the power iteration runs instead on each node's
+// d x d covariance, formed once on the fp64 matrix cores (the covariance path
+// below).  The split is an exact radix select on the fp64 projections (64-bit
+// order-preserving keys, ties broken by position = token index) followed by a
+// stable partition.
 #include <utility>
 
 #include "mcs_common.h"
