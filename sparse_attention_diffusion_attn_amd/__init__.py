@@ -12,6 +12,12 @@ Reuse step:   o = sparse_attn(q_t, k_t, v_t, perm, kv_idx, r, ...)
 Selection variants of the oracle analysis (block oracle, vanilla BSA):
               kv_idx, kv_count = block_select(...);  r = residual_counts(...);
               o = sparse_attn_counts(...)
+Grouping comparator (size-balanced k-means): perm = group_kmeans(...)
+
+group, anchor_select, residual, sparse_attn and dense_attn also take Q, K, V
+and the output as strided [B, H, n_pad, d] views with contiguous rows (e.g. a
+[B, N, H, d] tensor transposed, or slices of a fused QKV projection); they are
+then passed to the library's `_strided` calls.
 """
 from __future__ import annotations
 
