@@ -150,13 +150,14 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   issue(0);
   if (ntiles > 1) fetch_idx(1);
 
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vm0();
-    __syncthreads();
+  // One key tile: the copies of tile t+1 go to kdst_n (the other buffer)
+  // while kbuf/vbuf (this tile's K and V) are read.  The three pointers are
+  // restrict-qualified: the compiler then knows that the LDS reads cannot
+  // alias the copies in flight, and does not make the transposing V reads
+  // wait for those copies (it would otherwise insert a vmcnt(0) before them).
+  auto tile = [&](int t, char* __restrict__ kdst_n, const char* __restrict__ kbuf,
+                  const char* __restrict__ vbuf) __attribute__((always_inline)) {
     const bool more = t + 1 < ntiles;
-    char* kdst_n = lds + ((t + 1) & 1) * 2 * TILE + w * IPW * 1024;
-    const char* kbuf = lds + (t & 1) * 2 * TILE;
-    const char* vbuf = kbuf + TILE;
 
     // S^T = K . Q^T for the 64 keys of this tile (two 32-key blocks).  The K
     // operands of k-step kk+1 are read while the products of kk run, and
@@ -255,14 +256,23 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
       lrun += la + lb;
     }
 
-    // O^T += V^T . P^T.  The transposing reads are issued from inline asm
-    // (with their wait inside the same block) so that the compiler does not
-    // make them wait for the global->LDS copies of the next tile, which write
-    // the other buffer.
+    // O^T += V^T . P^T, 16 keys (one k-step) per block u; the V operands of
+    // block u+1 are read while the products of block u run.
+    auto read_v = [&](i32x2* va, int u) {
+#pragma unroll
+      for (int T = 0; T < NPL; ++T) {
+        va[2 * T] = tr_read(vbuf + voff_a + u * 1024 + T * 4096);
+        va[2 * T + 1] = tr_read(vbuf + voff_b + u * 1024 + T * 4096);
+      }
+    };
+    i32x2 vcur[2 * NPL];
+    read_v(vcur, 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       i32x2 va[2 * NPL];
-      tr_read_planes<NPL>(va, vbuf + voff_a + u * 1024, vbuf + voff_b + u * 1024);
+#pragma unroll
+      for (int i = 0; i < 2 * NPL; ++i) va[i] = vcur[i];
+      if (u + 1 < 4) read_v(vcur, u + 1);
 #pragma unroll
       for (int T = 0; T < NPL; ++T) {
         const bf16x8 a = __builtin_bit_cast(bf16x8, (i32x4){va[2 * T][0], va[2 * T][1],
@@ -270,6 +280,13 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
         o[T] = mfma32(a, pb[u], o[T]);
       }
     }
+  };
+
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vm0();
+    __syncthreads();
+    tile(t, lds + ((t + 1) & 1) * 2 * TILE + w * IPW * 1024, lds + (t & 1) * 2 * TILE,
+         lds + (t & 1) * 2 * TILE + TILE);
   }
 
   // ---- epilogue ----

@@ -65,41 +65,13 @@ __device__ __forceinline__ float sum_xor32(float x) {
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Transposing LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
 // j receives element (j % 4) of the 8-byte rows addressed by lanes j/4, j/4+4,
-// j/4+8 and j/4+12.  For every column plane T (4 KiB apart) this reads rows at
-// `pa` and at `pb` into out[2T] and out[2T+1], and waits for them before the
-// block ends (so no read is still in flight when its registers are used).
-template <int NPL>
-__device__ __forceinline__ void tr_read_planes(i32x2* out, const char* pa, const char* pb) {
-  const uint32_t a = (uint32_t)(uintptr_t)pa;
-  const uint32_t b = (uint32_t)(uintptr_t)pb;
-  if constexpr (NPL == 4) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:8192\n\t"
-        "ds_read_b64_tr_b16 %5, %9 offset:8192\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:12288\n\t"
-        "ds_read_b64_tr_b16 %7, %9 offset:12288\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]),
-          "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7])
-        : "v"(a), "v"(b)
-        : "memory");
-  } else {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4\n\t"
-        "ds_read_b64_tr_b16 %1, %5\n\t"
-        "ds_read_b64_tr_b16 %2, %4 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %3, %5 offset:4096\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
-        : "v"(a), "v"(b)
-        : "memory");
-  }
+// j/4+8 and j/4+12.
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ i32x2 tr_read(const char* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)p;
+  return __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a));
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs.  Map dispatch index i to a
