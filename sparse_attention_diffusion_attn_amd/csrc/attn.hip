@@ -194,6 +194,17 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // The V operands of the whole tile (four 16-key blocks) are read right
+    // after the QK^T products: they do not depend on the softmax, which then
+    // hides their latency.
+    i32x2 vall[4][2 * NPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int T = 0; T < NPL; ++T) {
+        vall[u][2 * T] = tr_read(vbuf + voff_a + u * 1024 + T * 4096);
+        vall[u][2 * T + 1] = tr_read(vbuf + voff_b + u * 1024 + T * 4096);
+      }
     if (t + 2 < ntiles) fetch_idx(t + 2);
 
     // mask keys past the end in the last tile (slot s holds key
@@ -256,23 +267,10 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
       lrun += la + lb;
     }
 
-    // O^T += V^T . P^T, 16 keys (one k-step) per block u; the V operands of
-    // block u+1 are read while the products of block u run.
-    auto read_v = [&](i32x2* va, int u) {
-#pragma unroll
-      for (int T = 0; T < NPL; ++T) {
-        va[2 * T] = tr_read(vbuf + voff_a + u * 1024 + T * 4096);
-        va[2 * T + 1] = tr_read(vbuf + voff_b + u * 1024 + T * 4096);
-      }
-    };
-    i32x2 vcur[2 * NPL];
-    read_v(vcur, 0);
+    // O^T += V^T . P^T, 16 keys (one k-step) per block u.
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      i32x2 va[2 * NPL];
-#pragma unroll
-      for (int i = 0; i < 2 * NPL; ++i) va[i] = vcur[i];
-      if (u + 1 < 4) read_v(vcur, u + 1);
+      const i32x2* va = vall[u];
 #pragma unroll
       for (int T = 0; T < NPL; ++T) {
         const bf16x8 a = __builtin_bit_cast(bf16x8, (i32x4){va[2 * T][0], va[2 * T][1],
