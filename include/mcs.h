@@ -44,6 +44,18 @@
  * between calls; the metadata (perm, kv_idx, R) is ordinary caller memory that
  * may be cached, offloaded to the host or reloaded between steps.
  *
+ * Device data is not validated (checking it would cost a pass over it):
+ *   - perm must be a permutation of 0 .. n_pad-1 per head, as mcs_group
+ *     writes it.  Its entries address query and output rows directly, so an
+ *     entry outside 0 .. n_pad-1 makes a kernel read and write out of bounds.
+ *   - kv_idx entries must lie in 0 .. n_valid-1.  The K/V gathers are
+ *     buffer loads bounded by the head's rows, so an entry outside that range
+ *     reads a padding row, another row of the head or zeros, never memory
+ *     outside the head, and only the result is wrong.  Ascending order is what
+ *     the selection writes and what keeps the gathers sweeping forward;
+ *     another order gives the same result up to rounding, and a repeated key
+ *     is counted twice.
+ *
  * Asynchrony: every call only enqueues work on `stream` (a hipStream_t; NULL is
  * the default stream) and returns.  Outputs are valid once the stream reaches
  * that point.  Calls on one stream run in order.
