@@ -746,7 +746,9 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   constexpr int NTH = 256;
   __shared__ double sig[D * D];
   __shared__ double vec[D];
-  __shared__ double red[NTH];
+  __shared__ double mus[D];
+  __shared__ double red[2];
+  __shared__ double half[64];
   __shared__ double vmag[D];
   __shared__ int vidx[D];
   const int G = p.groups;
@@ -755,28 +757,28 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   const int slot = blockIdx.x - bh * slots;
   int s, m;
   if (!node_of_slot(G, p.level, slot, s, m) || m < 2) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   // X^T X of the node (the chunk sums are already in chunk 0), centred and
-  // mirrored to a full matrix
+  // mirrored to a full matrix.  Pass k handles upper tile k (256 elements, one
+  // per thread), so every load of the pass is independent of the others.
   const double* src = p.gram + (int64_t)(bh * slots + slot) * p.nch * (NT * 256);
   double* mu = p.mu + ((size_t)bh * G + s) * D;
   double* vv = p.vec + ((size_t)bh * G + s) * D;
   const double n = (double)(m * C);
-  for (int e = tid; e < NT * 256; e += NTH) {
-    const double a = src[e];
-    const int t = e >> 8, li = (e >> 4) & 15, lj = e & 15;
-    int ti = 0, len = DT, tt = t;
-    while (tt >= len) {
-      tt -= len;
-      ++ti;
-      --len;
-    }
-    const int i = 16 * ti + li, jj = 16 * (ti + tt) + lj;
-    const double c = a - n * mu[i] * mu[jj];
+  if (tid < D) {
+    mus[tid] = mu[tid];
+    vec[tid] = 1.0 / sqrt((double)D);
+  }
+  __syncthreads();
+  const int li = tid >> 4, lj = tid & 15;
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    const double a = src[k * 256 + tid];
+    const int i = 16 * gram_tile_i<DT>(k) + li, jj = 16 * gram_tile_j<DT>(k) + lj;
+    const double c = a - n * mus[i] * mus[jj];
     sig[i * D + jj] = c;
     sig[jj * D + i] = c;
   }
-  if (tid < D) vec[tid] = 1.0 / sqrt((double)D);
   __syncthreads();
   for (int it = 0; it < p.power_iters; ++it) {
     // w_i = sum_j Sigma_ij v_j, read down column i (Sigma is stored symmetric,
@@ -786,14 +788,22 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
     if (tid < D) {
       for (int jj = 0; jj < D; ++jj) w = __builtin_fma(sig[jj * D + tid], vec[jj], w);
     }
-    red[tid] = (tid < D) ? w * w : 0.0;
-    __syncthreads();
-    for (int o = NTH / 2; o > 0; o >>= 1) {
-      if (tid < o) red[tid] += red[tid + o];
+    // |w|^2 summed as a pairwise tree: element i meets i + D/2, then i + D/4,
+    // ..., i + 1 (the first halving across the two waves through LDS, the
+    // rest inside wave 0 by lane shifts)
+    double q = (tid < D) ? w * w : 0.0;
+    if constexpr (D == 128) {
+      if (tid >= 64 && tid < 128) half[lane] = q;
       __syncthreads();
+      if (tid < 64) q += half[lane];
     }
-    const double nrm2 = red[0];
+    if (tid < 64) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) q += __shfl_down(q, o, 64);
+      if (tid == 0) red[0] = q;
+    }
     __syncthreads();
+    const double nrm2 = red[0];
     if (tid < D && nrm2 > 0.0) vec[tid] = w / sqrt(nrm2);
     __syncthreads();
   }
