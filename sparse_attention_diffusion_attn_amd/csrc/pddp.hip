@@ -771,13 +771,15 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   }
   __syncthreads();
   const int li = tid >> 4, lj = tid & 15;
+  int ti = 0, tj = 0;  // tile k = (ti, tj), upper tiles in row-major order
 #pragma unroll
   for (int k = 0; k < NT; ++k) {
     const double a = src[k * 256 + tid];
-    const int i = 16 * gram_tile_i<DT>(k) + li, jj = 16 * gram_tile_j<DT>(k) + lj;
+    const int i = 16 * ti + li, jj = 16 * tj + lj;
     const double c = a - n * mus[i] * mus[jj];
     sig[i * D + jj] = c;
     sig[jj * D + i] = c;
+    if (++tj == DT) tj = ++ti;
   }
   __syncthreads();
   for (int it = 0; it < p.power_iters; ++it) {
