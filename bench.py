@@ -9,7 +9,7 @@ density, k = 8190, 1 anchor + 4 reuse steps).
 
 Headline metric: effective TFLOP/s of the reuse-step sparse attention
 (4*B*H*N_pad*k*d executed flops / kernel time, HIP events on the launch
-stream), and the achieved fraction of the ideal 1/s speed-up over this build's
+stream), and the achieved fraction of the ideal 1/s speed-up over the library's
 own dense kernel (mcs_dense_attn) at the same shape: (k/N) * t_dense / t_sparse.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 480p]
@@ -106,8 +106,8 @@ def cpu_baseline(cfg, q, k, v, perm, kv, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "heads shard across GPUs with no exchange, which is not exercised here.", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
+              "heads would shard across GPUs with no exchange, which is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
