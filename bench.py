@@ -95,12 +95,18 @@ def cpu_baseline(cfg, q, k, v, perm, kv, budget_s):
             if time.perf_counter() - t0 > budget_s:
                 break
     dt = time.perf_counter() - t0
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {"value": flops_per_group * done / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"fp64 oracle sparse attention of {done} query groups (C={cfg.group_size}, "
                       f"k={cfg.topk}, d={cfg.head_dim}) from the first {heads} head(s) of the same layer "
                       f"(reuse step 1, the GPU's metadata), one thread, "
-                      f"{dt:.1f} s; host {platform.processor() or platform.machine()}, "
-                      f"{os.cpu_count()} logical CPUs visible"}
+                      f"{dt:.1f} s; host {model}, {os.cpu_count()} logical CPUs, {usable} usable"}
 
 
 def main():
