@@ -31,8 +31,14 @@ constexpr float kLazyLog2 = 8.0f;
 __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <int D, int C, int MODE>
-__global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
-  constexpr int NW = C / 32;            // wavefronts, 32 query rows each
+__global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
+  // Four wavefronts.  C = 128: one per 32-row block of the group.  C = 64:
+  // two per 32-row block, one per half of every key tile (SPLIT); their
+  // partial softmax states are merged in the epilogue.  Either way a CU holds
+  // two workgroups, eight wavefronts.
+  static_assert(C == 128 || C == 64, "group size");
+  constexpr bool SPLIT = (C == 64);
+  constexpr int NW = 4;
   constexpr int KT = 64;                // keys per tile
   constexpr int NPL = D / 32;           // column planes per tile (4 KiB each)
   constexpr int TILE = NPL * 4096;      // bytes per matrix tile
@@ -47,6 +53,8 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ql = lane & 31;
   const int h = lane >> 5;
+  const int rb = SPLIT ? (w & 1) : w;   // this wavefront's 32-row block
+  const int kh = SPLIT ? (w >> 1) : 0;  // its half of each key tile (SPLIT)
 
   const int G = p.groups;
   const int work = xcd_remap(blockIdx.x, gridDim.x);
@@ -57,7 +65,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   const uint16_t* Vb = p.v + head_offset(p.sv, bh, p.heads);
 
   // ---- query rows of this lane (B operand of S^T, resident in VGPRs) ----
-  const int qpos = g * C + 32 * w + ql;
+  const int qpos = g * C + 32 * rb + ql;
   const int qrow = (MODE == ATTN_DENSE) ? qpos : p.perm[(size_t)bh * p.n_pad + qpos];
   bf16x8 qreg[KS];
 #pragma unroll
@@ -165,19 +173,20 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
     f32x16 s0, s1;
 #pragma unroll
     for (int j = 0; j < 16; ++j) { s0[j] = 0.f; s1[j] = 0.f; }
-    bf16x8 a0 = *(const bf16x8*)(kbuf + koff_e);
-    bf16x8 a1 = *(const bf16x8*)(kbuf + koff_e + 2048);
+    // (SPLIT: only the 32 keys of this wavefront's half, in s0)
+    bf16x8 a0 = *(const bf16x8*)(kbuf + koff_e + kh * 2048);
+    bf16x8 a1 = SPLIT ? a0 : *(const bf16x8*)(kbuf + koff_e + 2048);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       bf16x8 n0 = a0, n1 = a1;
       if (kk + 1 < KS) {
         const char* kp = kbuf + (((kk + 1) & 1) ? koff_o : koff_e) + ((kk + 1) >> 1) * 4096;
-        n0 = *(const bf16x8*)(kp);
-        n1 = *(const bf16x8*)(kp + 2048);
+        n0 = *(const bf16x8*)(kp + kh * 2048);
+        if (!SPLIT) n1 = *(const bf16x8*)(kp + 2048);
       }
       __builtin_amdgcn_sched_barrier(0);
       s0 = mfma32(a0, qreg[kk], s0);
-      s1 = mfma32(a1, qreg[kk], s1);
+      if (!SPLIT) s1 = mfma32(a1, qreg[kk], s1);
       a0 = n0;
       a1 = n1;
       if (more) {
@@ -197,13 +206,15 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
     // The V operands of the whole tile (four 16-key blocks) are read right
     // after the QK^T products: they do not depend on the softmax, which then
     // hides their latency.
-    i32x2 vall[4][2 * NPL];
+    constexpr int NU = SPLIT ? 2 : 4;   // 16-key blocks of this wavefront
+    i32x2 vall[NU][2 * NPL];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int T = 0; T < NPL; ++T) {
-        vall[u][2 * T] = tr_read(vbuf + voff_a + u * 1024 + T * 4096);
-        vall[u][2 * T + 1] = tr_read(vbuf + voff_b + u * 1024 + T * 4096);
+        const int ub = (SPLIT ? 2 * kh : 0) + u;
+        vall[u][2 * T] = tr_read(vbuf + voff_a + ub * 1024 + T * 4096);
+        vall[u][2 * T + 1] = tr_read(vbuf + voff_b + ub * 1024 + T * 4096);
       }
     if (t + 2 < ntiles) fetch_idx(t + 2);
 
@@ -215,8 +226,8 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
       for (int j = 0; j < 16; ++j) {
         const int slot = 8 * (j >> 2) + 4 * h + (j & 3);
         const int key = 4 * (slot & 15) + (slot >> 4);
-        if (key >= lim) s0[j] = -INFINITY;
-        if (key + 2 >= lim) s1[j] = -INFINITY;
+        if (key + 2 * kh >= lim) s0[j] = -INFINITY;
+        if (!SPLIT && key + 2 >= lim) s1[j] = -INFINITY;
       }
     }
 
@@ -228,8 +239,10 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
     float mx = s0[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s0[j]);
+    if (!SPLIT) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s1[j]);
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s1[j]);
+    }
     mx = max_xor32(mx);
     const bool raise = (mx - mrun) * c2 > kLazyLog2;
     if (__any(raise)) {
@@ -242,21 +255,25 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[T][j] *= alpha;
     }
-    const float mc = mrun * c2;
-    bf16x8 pb[4];
+    // (SPLIT: a half that has seen no valid key yet keeps mrun = -inf; its
+    // probabilities are then exp2(-inf) = 0 rather than NaN)
+    const float mc = (SPLIT && mrun == -INFINITY) ? 0.f : mrun * c2;
+    bf16x8 pb[NU];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[j], c2, -mc));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[j], c2, -mc));
       pb[j >> 3][j & 7] = (__bf16)e0;
-      pb[2 + (j >> 3)][j & 7] = (__bf16)e1;
+      if (!SPLIT) {
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[j], c2, -mc));
+        pb[(2 + (j >> 3)) % NU][j & 7] = (__bf16)e1;
+      }
     }
     // row sum of the bf16 probabilities the PV product uses (so numerator and
     // denominator see the same rounded weights), two per dot2 instruction
     {
       float la = 0.f, lb = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < NU; ++q) {
         const bf16x2 p01 = {pb[q][0], pb[q][1]}, p23 = {pb[q][2], pb[q][3]};
         const bf16x2 p45 = {pb[q][4], pb[q][5]}, p67 = {pb[q][6], pb[q][7]};
         la = __builtin_amdgcn_fdot2_f32_bf16(p01, kOnes2, la, false);
@@ -269,7 +286,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
 
     // O^T += V^T . P^T, 16 keys (one k-step) per block u.
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const i32x2* va = vall[u];
 #pragma unroll
       for (int T = 0; T < NPL; ++T) {
@@ -288,7 +305,37 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
   }
 
   // ---- epilogue ----
-  const float lsum = sum_xor32(lrun);
+  float lsum = sum_xor32(lrun);
+  if constexpr (SPLIT) {
+    // merge the two key halves of each row block: the kh = 1 wavefront hands
+    // its running max, row sum and O to the kh = 0 one through LDS (the tile
+    // buffers are free once every wavefront has passed the barrier; no copy is
+    // in flight after the last tile), and the kh = 0 wavefront rescales both
+    // to the common max
+    constexpr int NV = NPL * 16 + 2;    // values per lane
+    float* xo = reinterpret_cast<float*>(lds) + rb * NV * 64 + lane;
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int T = 0; T < NPL; ++T)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) xo[(T * 16 + j) * 64] = o[T][j];
+      xo[(NPL * 16) * 64] = mrun;
+      xo[(NPL * 16 + 1) * 64] = lsum;
+    }
+    __syncthreads();
+    if (kh == 1) return;                // no barrier follows
+    const float m1 = xo[(NPL * 16) * 64], l1 = xo[(NPL * 16 + 1) * 64];
+    const float m = fmaxf(mrun, m1);    // mrun is finite: key 0 lies in half 0
+    const float f0 = __builtin_amdgcn_exp2f((mrun - m) * c2);
+    const float f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c2);
+#pragma unroll
+    for (int T = 0; T < NPL; ++T)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[T][j] = o[T][j] * f0 + xo[(T * 16 + j) * 64] * f1;
+    lsum = lsum * f0 + l1 * f1;
+    mrun = m;
+  }
   const float inv = 1.f / lsum;
   const bool valid = qrow < p.n_valid;
   uint16_t* Ob = p.out + head_offset(p.so, bh, p.heads) + (int64_t)qrow * p.so.n;
@@ -334,7 +381,7 @@ __global__ __launch_bounds__(2 * C) void attn_kernel(AttnParams p) {
 template <int D, int C, int MODE>
 static hipError_t launch_one(const AttnParams& p, hipStream_t s) {
   const int64_t items = p.bh * (int64_t)p.groups;
-  hipLaunchKernelGGL((attn_kernel<D, C, MODE>), dim3((unsigned)items), dim3(2 * C), 0, s, p);
+  hipLaunchKernelGGL((attn_kernel<D, C, MODE>), dim3((unsigned)items), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
