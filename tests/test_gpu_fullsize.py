@@ -39,12 +39,19 @@ def data_for(cfg):
                       cfg.drift, cfg.seed)
 
 
-FULL = ["480p", "3d", "wan720p", "hunyuan720p_15", "hunyuan720p_25"]
+FULL = ["480p", "3d", "wan720p", "hunyuan720p_15", "hunyuan720p_25", "480p_c64"]
+# the 480p layer with groups of 64 queries (the split-key-tile attention path)
+EXTRA = {"480p_c64": sd.custom("480p_c64", heads=24, n_valid=32760, head_dim=128, group_size=64,
+                               density_pct=25, n_clusters=64)}
+
+
+def config(name):
+    return EXTRA[name] if name in EXTRA else sd.CONFIGS[name]
 
 
 @pytest.mark.parametrize("name", FULL)
 def test_fullsize_pipeline_sampled(mcs, name):
-    cfg = sd.CONFIGS[name]
+    cfg = config(name)
     print(f"\n[{name}] H{cfg.heads} N{cfg.n_valid}->{cfg.n_pad} d{cfg.head_dim} C{cfg.group_size} k{cfg.topk}",
           flush=True)
     (q, k, v), (qt, kt, vt) = data_for(cfg)
