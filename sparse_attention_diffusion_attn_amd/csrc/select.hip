@@ -22,8 +22,13 @@
 namespace mcs {
 
 template <int D, int C>
-__global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
-  constexpr int NW = C / 32;
+__global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
+  // Four wavefronts.  C = 128: one per 32-query block.  C = 64 (SPLIT): two
+  // per 32-query block, one per 32-key half of every tile.
+  static_assert(C == 128 || C == 64, "group size");
+  constexpr bool SPLIT = (C == 64);
+  constexpr int NW = 4;
+  constexpr int NRB = C / 32;          // 32-query blocks
   constexpr int KT = 64;
   constexpr int NPL = D / 32;
   constexpr int TILE = NPL * 4096;
@@ -32,13 +37,15 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
   constexpr int KS = D / 16;
 
   __shared__ __attribute__((aligned(1024))) char lds[2 * TILE];
-  __shared__ float red[2][NW][KT];
+  __shared__ float red[2][NRB][KT];
   __shared__ int hist_s[1024];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ql = lane & 31;
   const int h = lane >> 5;
+  const int rb = SPLIT ? (w & 1) : w;   // this wavefront's 32-query block
+  const int kh = SPLIT ? (w >> 1) : 0;  // its 32-key half of each tile (SPLIT)
 
   const int G = p.groups;
   const int work = xcd_remap(blockIdx.x, gridDim.x);
@@ -49,19 +56,19 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
   const uint16_t* Kb = p.k + head_offset(p.sk, bh, p.heads);
   const int32_t* permb = p.perm + (size_t)bh * p.n_pad + (size_t)g * C;
 
-  // A operand of S = Q K^T: this lane's query row 32w + ql.
-  const int qrow = permb[32 * w + ql];
+  // A operand of S = Q K^T: this lane's query row 32rb + ql.
+  const int qrow = permb[32 * rb + ql];
   bf16x8 qreg[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
     qreg[kk] = *(const bf16x8*)(Qb + (int64_t)qrow * p.sq.n + 16 * kk + 8 * h);
 
-  // Accumulator j of S holds query 32w + 8(j/4) + 4h + (j%4): its lse in log2
+  // Accumulator j of S holds query 32rb + 8(j/4) + 4h + (j%4): its lse in log2
   // units (+inf for padded queries, whose terms then vanish).
   float lse2[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int r = permb[32 * w + 8 * (j >> 2) + 4 * h + (j & 3)];
+    const int r = permb[32 * rb + 8 * (j >> 2) + 4 * h + (j & 3)];
     lse2[j] = (r < p.n_valid) ? p.lse[(size_t)bh * p.n_pad + r] * kLog2e : INFINITY;
   }
 
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
       const int key = t * KT + threadIdx.x;
       float a = red[t & 1][0][threadIdx.x];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) a += red[t & 1][ww][threadIdx.x];
+      for (int ww = 1; ww < NRB; ++ww) a += red[t & 1][ww][threadIdx.x];
       if (key < nk) {
         out[key] = a;
         if (want_hist) atomicAdd(&hist_s[__float_as_uint(a) >> 22], 1);
@@ -128,10 +135,12 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const char* kp = kbuf + ((kk & 1) ? koff_o : koff_e) + (kk >> 1) * 4096;
-      const bf16x8 b0 = *(const bf16x8*)(kp);
-      const bf16x8 b1 = *(const bf16x8*)(kp + 2048);
+      const bf16x8 b0 = *(const bf16x8*)(kp + kh * 2048);
       s0 = mfma32(qreg[kk], b0, s0);
-      s1 = mfma32(qreg[kk], b1, s1);
+      if (!SPLIT) {
+        const bf16x8 b1 = *(const bf16x8*)(kp + 2048);
+        s1 = mfma32(qreg[kk], b1, s1);
+      }
       if (more) {
         constexpr int PER = (IPW + KS - 1) / KS;
 #pragma unroll
@@ -147,13 +156,13 @@ __global__ __launch_bounds__(2 * C) void score_kernel(ScoreParams p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(s0[j], c2, -lse2[j]));
-      a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(s1[j], c2, -lse2[j]));
+      if (!SPLIT) a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(s1[j], c2, -lse2[j]));
     }
     a0 = sum_xor32(a0);
-    a1 = sum_xor32(a1);
+    if (!SPLIT) a1 = sum_xor32(a1);
     if (h == 0) {
-      red[t & 1][w][ql] = a0;
-      red[t & 1][w][32 + ql] = a1;
+      red[t & 1][rb][32 * kh + ql] = a0;
+      if (!SPLIT) red[t & 1][rb][32 + ql] = a1;
     }
   }
   __syncthreads();
@@ -307,7 +316,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
 template <int D, int C>
 static hipError_t launch_scores_t(const ScoreParams& p, hipStream_t s) {
   const int64_t items = p.bh_count * (int64_t)p.groups;
-  hipLaunchKernelGGL((score_kernel<D, C>), dim3((unsigned)items), dim3(2 * C), 0, s, p);
+  hipLaunchKernelGGL((score_kernel<D, C>), dim3((unsigned)items), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
