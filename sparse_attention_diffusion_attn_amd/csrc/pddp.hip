@@ -743,7 +743,6 @@ __global__ __launch_bounds__(256) void pddp_gram_sum_kernel(PddpParams p) {
 template <int D, int C>
 __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   constexpr int DT = D / 16, NT = DT * (DT + 1) / 2;
-  constexpr int NTH = 256;
   __shared__ double sig[D * D];
   __shared__ double vec[D];
   __shared__ double mus[D];
