@@ -6,8 +6,9 @@
 // The dense mode is the dense baseline and anchor pass 1; the residual mode
 // writes R = O_full - SparseAttn(...) at the anchor.
 //
-// One workgroup per (head, query group): C/32 wavefronts, each owning 32 query
-// rows.  Key/value tiles of 64 rows are gathered by index with 16-byte
+// One workgroup per (head, query group), four wavefronts: for C = 128 each owns
+// 32 query rows; for C = 64 two share each 32-row block, one per 32-key half of
+// every tile.  Key/value tiles of 64 rows are gathered by index with 16-byte
 // buffer->LDS copies into a double-buffered LDS tile (column planes, chunks
 // permuted per row against bank conflicts).  The copies of tile t+1 are
 // issued one per k-step of tile t's QK^T product (spread out, so the vector
