@@ -473,7 +473,18 @@ __global__ __launch_bounds__(512) void pddp_split_kernel(PddpParams p) {
     const uint64_t dmask = (1ull << widths[pass]) - 1ull;
     for (int b = tid; b < NBIN; b += NT) hist[b] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += NT) {
+    // eight independent loads in flight per thread: the pass is bound by their
+    // latency, not by the LDS atomics
+    int i = tid;
+    for (; i + 7 * NT < n; i += 8 * NT) {
+      uint64_t u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[e] = order_key(pr[i + e * NT]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((u[e] & pmask) == prefix) atomicAdd(&hist[(int)((u[e] >> sh) & dmask)], 1);
+    }
+    for (; i < n; i += NT) {
       const uint64_t u = order_key(pr[i]);
       if ((u & pmask) == prefix) atomicAdd(&hist[(int)((u >> sh) & dmask)], 1);
     }
