@@ -239,7 +239,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     } else {
       for (int b = tid; b < NBIN; b += NT) hist[b] = 0;
       __syncthreads();
-      for (int j = tid; j < n; j += NT) {
+      // eight independent loads in flight per thread
+      int j = tid;
+      for (; j + 7 * NT < n; j += 8 * NT) {
+        uint32_t u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = key(a[j + e * NT]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((u[e] & pmask) == prefix) atomicAdd(&hist[(u[e] >> sh) & dmask], 1);
+      }
+      for (; j < n; j += NT) {
         const uint32_t u = key(a[j]);
         if ((u & pmask) == prefix) atomicAdd(&hist[(u >> sh) & dmask], 1);
       }
