@@ -4,15 +4,19 @@
 One step = one pass of the whole hot path over one synthetic layer: the anchor
 step (mcs_group -> mcs_anchor_select -> mcs_residual) followed by the layer's
 reuse steps (mcs_sparse_attn on drifted Q/K/V, cached metadata).  Default
-workload: the 480p video-DiT layer (B1 H24 N32760 -> 32768, d128, C128, 25%
-density, k = 8190, 1 anchor + 4 reuse steps).
+workload: the HunyuanVideo-13B-shaped 720p layer (B1 H24 N118800 -> 118912,
+d128, C128, 25% density, k = 29700, 1 anchor + 8 reuse steps); the same layer
+at 15% density (k = 17820: a second selection on the same inputs and groups)
+is measured beside it.  To keep the CPU-side input generation short, the reuse
+steps cycle over `--reuse-inputs` distinct drifted inputs (default 2) instead
+of drawing one per step; the kernels' work does not depend on the values.
 
 Headline metric: effective TFLOP/s of the reuse-step sparse attention
 (4*B*H*N_pad*k*d executed flops / kernel time, HIP events on the launch
 stream), and the achieved fraction of the ideal 1/s speed-up over the library's
 own dense kernel (mcs_dense_attn) at the same shape: (k/N) * t_dense / t_sparse.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 480p]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config hunyuan720p_25]
 """
 from __future__ import annotations
 
@@ -37,7 +41,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="480p")
+    ap.add_argument("--config", default="hunyuan720p_25")
+    ap.add_argument("--also-density", type=int, default=None,
+                    help="second density (percent) measured on the same inputs "
+                         "(default: 15 for the 25%% Hunyuan layer, none otherwise)")
+    ap.add_argument("--reuse-inputs", type=int, default=2,
+                    help="distinct drifted reuse-step inputs the reuse steps cycle over")
     ap.add_argument("--ratio-reps", type=int, default=10, help="reps of the dense-vs-sparse timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
@@ -56,10 +65,11 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_src_hash):
+def load_traffic(config, kernel_src_hash):
     """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE and
-    WRITE_SIZE), stored with the hash of the kernel source it was taken on."""
-    path = os.path.join(ROOT, "profiles", "sparse_attn_480p_traffic.json")
+    WRITE_SIZE) on this config's sparse launch, stored with the hash of the
+    kernel source it was taken on."""
+    path = os.path.join(ROOT, "profiles", f"sparse_attn_{config}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -116,6 +126,8 @@ def main():
               "heads would shard across GPUs with no exchange, which is not implemented.", file=sys.stderr)
         sys.exit(2)
 
+    import dataclasses
+
     import torch
     import sparse_attention_diffusion_attn_amd as mcs
     import synthdata as sd
@@ -125,16 +137,20 @@ def main():
     dev = torch.device("cuda:0")
     cfg = sd.CONFIGS[args.config]
     if args.reuse is not None:
-        import dataclasses
         cfg = dataclasses.replace(cfg, n_reuse=args.reuse)
+    also = args.also_density
+    if also is None and args.config == "hunyuan720p_25":
+        also = 15
     B, H, nv, n_pad, d, C, k = cfg.batch, cfg.heads, cfg.n_valid, cfg.n_pad, cfg.head_dim, cfg.group_size, cfg.topk
     sc = cfg.scale
+    n_inputs = max(1, min(args.reuse_inputs, cfg.n_reuse))
     t_gen = time.perf_counter()
-    steps_cpu = sd.generate(cfg)
-    print(f"# generated {len(steps_cpu)} steps of {cfg.name} in {time.perf_counter() - t_gen:.1f} s",
-          file=sys.stderr, flush=True)
+    steps_cpu = sd.generate(cfg, steps=1 + n_inputs)
+    print(f"# generated the anchor and {n_inputs} reuse-step inputs of {cfg.name} in "
+          f"{time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     steps = [tuple(t.to(dev) for t in s) for s in steps_cpu]
     q0, k0, v0 = steps[0]
+    reuse_in = [steps[1 + i % n_inputs] for i in range(cfg.n_reuse)]
     dims = mcs.make_dims(B, H, nv, n_pad, d, C)
     G = cfg.groups
     perm = torch.empty((B, H, n_pad), dtype=torch.int32, device=dev)
@@ -142,7 +158,7 @@ def main():
     lse = torch.empty((B, H, n_pad), dtype=torch.float32, device=dev)
     kv = torch.empty((B, H, G, k), dtype=torch.int32, device=dev)
     r = torch.empty_like(q0)
-    outs = [torch.empty_like(q0) for _ in steps[1:]]
+    outs = [torch.empty_like(q0) for _ in range(n_inputs)]
     ws_g = torch.empty(mcs.group_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(mcs.anchor_select_workspace_bytes(dims, k), dtype=torch.uint8, device=dev)
 
@@ -158,8 +174,8 @@ def main():
         e = ev(); e.record(); marks.append(e)
         mcs.residual(q0, k0, v0, perm, kv, o_full, nv, C, sc, r=r)
         e = ev(); e.record(); marks.append(e)
-        for (qt, kt, vt), o in zip(steps[1:], outs):
-            mcs.sparse_attn(qt, kt, vt, perm, kv, r, nv, C, sc, o=o)
+        for i, (qt, kt, vt) in enumerate(reuse_in):
+            mcs.sparse_attn(qt, kt, vt, perm, kv, r, nv, C, sc, o=outs[i % n_inputs])
             e = ev(); e.record(); marks.append(e)
         record.append(marks)
 
@@ -179,7 +195,7 @@ def main():
         torch.cuda.synchronize()
         for _ in range(args.steps):
             if args.only == "sparse":
-                mcs.sparse_attn(steps[1][0], steps[1][1], steps[1][2], perm, kv, r, nv, C, sc, o=outs[0])
+                mcs.sparse_attn(*steps[1], perm, kv, r, nv, C, sc, o=outs[0])
             elif args.only == "group":
                 mcs.group(q0, nv, C, cfg.power_iters, perm=perm, workspace=ws_g)
             elif args.only == "dense":
@@ -193,6 +209,7 @@ def main():
     for _ in range(args.warmup):
         one_step([])
     torch.cuda.synchronize()
+    print(f"# warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
     recs = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -231,39 +248,83 @@ def main():
     q1, k1, v1 = steps[1]
     o_d = torch.empty_like(q0)
 
-    def call(which):
-        if which == "dense":
-            mcs.dense_attn(q1, k1, v1, nv, C, sc, o=o_d, want_lse=False)
-        else:
-            mcs.sparse_attn(q1, k1, v1, perm, kv, r, nv, C, sc, o=outs[0])
+    def ratio(kv_sel, r_sel, topk):
+        def call(which):
+            if which == "dense":
+                mcs.dense_attn(q1, k1, v1, nv, C, sc, o=o_d, want_lse=False)
+            else:
+                mcs.sparse_attn(q1, k1, v1, perm, kv_sel, r_sel, nv, C, sc, o=outs[0])
 
-    def stream(which, n):
-        marks = []
-        for _ in range(n):
-            flush.sum()
-            a, b = ev(), ev()
-            a.record()
-            call(which)
-            b.record()
-            marks.append((a, b))
-        torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in marks]
+        def stream(which, n):
+            marks = []
+            for _ in range(n):
+                flush.sum()
+                a, b = ev(), ev()
+                a.record()
+                call(which)
+                b.record()
+                marks.append((a, b))
+            torch.cuda.synchronize()
+            return [a.elapsed_time(b) for a, b in marks]
 
-    density = k / nv
-    n_d = max(2, args.ratio_reps // 2)
-    n_s = max(2, round(n_d / density))
-    t_d, t_s = [], []
-    for which in ("dense", "sparse", "sparse", "dense"):
-        (t_d if which == "dense" else t_s).extend(stream(which, n_d if which == "dense" else n_s))
-    td, ts = statistics.median(t_d), statistics.median(t_s)
-    ideal_frac = density * td / ts
-    a_d, a_s = [], []
-    for _ in range(args.ratio_reps):
-        a_d.extend(stream("dense", 1))
-        a_s.extend(stream("sparse", 1))
-    ideal_frac_alt = density * statistics.median(a_d) / statistics.median(a_s)
+        density = topk / nv
+        n_d = max(2, args.ratio_reps // 2)
+        n_s = max(2, round(n_d / density))
+        t_d, t_s = [], []
+        for which in ("dense", "sparse", "sparse", "dense"):
+            (t_d if which == "dense" else t_s).extend(stream(which, n_d if which == "dense" else n_s))
+        td, ts = statistics.median(t_d), statistics.median(t_s)
+        a_d, a_s = [], []
+        for _ in range(args.ratio_reps):
+            a_d.extend(stream("dense", 1))
+            a_s.extend(stream("sparse", 1))
+        return {"density": density, "td": td, "ts": ts, "frac": density * td / ts,
+                "frac_alt": density * statistics.median(a_d) / statistics.median(a_s),
+                "td_min": min(t_d), "ts_min": min(t_s), "n_d": n_d, "n_s": n_s}
+
+    rt = ratio(kv, r, k)
+    td, ts = rt["td"], rt["ts"]
     dense_flops = 4.0 * B * H * n_pad * nv * d
     dense_tflops = dense_flops / (td * 1e-3) / 1e12
+    print(f"# ratio protocol at {cfg.density_pct}%: dense {td:.3f} ms, sparse {ts:.3f} ms, "
+          f"ideal-1/s fraction {rt['frac']:.4f}", file=sys.stderr, flush=True)
+
+    # the same layer at a second density: a second selection on the same
+    # inputs and groups, its residual, its reuse-step sparse attention
+    second = None
+    if also is not None:
+        k2 = (nv * also + 99) // 100
+        kv2 = torch.empty((B, H, G, k2), dtype=torch.int32, device=dev)
+        r2 = torch.empty_like(q0)
+        t_sel, t_res, t_sp = [], [], []
+        for rep in range(1 + args.steps):
+            m = [ev() for _ in range(4)]
+            m[0].record()
+            mcs.anchor_select(q0, k0, v0, perm, nv, C, k2, sc, o_full=o_full, lse=lse, kv_idx=kv2, workspace=ws_a)
+            m[1].record()
+            mcs.residual(q0, k0, v0, perm, kv2, o_full, nv, C, sc, r=r2)
+            m[2].record()
+            mcs.sparse_attn(*steps[1], perm, kv2, r2, nv, C, sc, o=outs[0])
+            m[3].record()
+            torch.cuda.synchronize()
+            if rep:
+                t_sel.append(m[0].elapsed_time(m[1]))
+                t_res.append(m[1].elapsed_time(m[2]))
+                t_sp.append(m[2].elapsed_time(m[3]))
+        rt2 = ratio(kv2, r2, k2)
+        t2 = statistics.mean(t_sp)
+        fl2 = 4.0 * B * H * n_pad * k2 * d
+        second = {"density_pct": also, "topk": k2,
+                  "sparse_ms_in_step": round(t2, 4),
+                  "effective_tflops": round(fl2 / (t2 * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(fl2 / (t2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "ideal_1_over_s_frac": round(rt2["frac"], 4),
+                  "ideal_1_over_s_frac_alternating": round(rt2["frac_alt"], 4),
+                  "dense_ms": round(rt2["td"], 4), "sparse_ms": round(rt2["ts"], 4),
+                  "stage_ms": {"anchor_select": round(statistics.mean(t_sel), 4),
+                               "residual": round(statistics.mean(t_res), 4)}}
+        print(f"# second density {also}%: sparse {t2:.3f} ms in step, ideal-1/s fraction {rt2['frac']:.4f}",
+              file=sys.stderr, flush=True)
 
     # torch's own fused attention at the same shape (valid tokens only), as a
     # sanity reference for the dense kernel; not a target
@@ -287,10 +348,11 @@ def main():
         print(f"# torch SDPA reference skipped: {e}", file=sys.stderr)
 
     kernel_hash = source_hash("attn.hip", "mcs_common.h")
-    traffic = load_traffic(kernel_hash)
+    traffic = load_traffic(args.config, kernel_hash)
+    kname = f"attn_kernel<{d},{C},1> (mcs_sparse_attn)"
     roofline = {"bound": "mfma", "achieved": round(eff_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(eff_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "attn_kernel<128,128,SPARSE> (mcs_sparse_attn)",
+                "traffic": traffic, "kernel": kname,
                 "flops_per_launch": sparse_flops, "avg_launch_ms": round(t_sparse_ms, 4),
                 "kernel_src_hash": kernel_hash}
     # the HBM side of the same launch: L2-fill bytes per launch (the traffic
@@ -326,18 +388,19 @@ def main():
         "data": "synthetic (seeded clustered Q/K, Gaussian V; no model weights)",
         "config": {
             "workload": f"{cfg.name} video-DiT attention layer: B{B} H{H} N{nv}->{n_pad} d{d} C{C} "
-                        f"density {cfg.density_pct}% (k={k}), 1 anchor + {cfg.n_reuse} reuse steps per step",
+                        f"density {cfg.density_pct}% (k={k}), 1 anchor + {cfg.n_reuse} reuse steps per step "
+                        f"(reuse inputs cycle over {n_inputs} drifted draws)",
             "batch": B, "heads": H, "n_valid": nv, "n_pad": n_pad, "head_dim": d, "group_size": C,
             "topk": k, "density_pct": cfg.density_pct, "reuse_steps": cfg.n_reuse,
-            "power_iters": cfg.power_iters, "parallelism": "single GPU"},
-        "ideal_1_over_s_frac": round(ideal_frac, 4),
-        "ratio_protocol": f"steady-state streams ({2 * n_d} dense, {2 * n_s} sparse calls), "
+            "reuse_inputs": n_inputs, "power_iters": cfg.power_iters, "parallelism": "single GPU"},
+        "ideal_1_over_s_frac": round(rt["frac"], 4),
+        "ratio_protocol": f"steady-state streams ({2 * rt['n_d']} dense, {2 * rt['n_s']} sparse calls), "
                           "512 MiB cache-evicting read before each call, per-call medians",
         "dense_ms": round(td, 4),
         "sparse_ms": round(ts, 4),
-        "ideal_1_over_s_frac_alternating": round(ideal_frac_alt, 4),
-        "dense_ms_min": round(min(t_d), 4),
-        "sparse_ms_min": round(min(t_s), 4),
+        "ideal_1_over_s_frac_alternating": round(rt["frac_alt"], 4),
+        "dense_ms_min": round(rt["td_min"], 4),
+        "sparse_ms_min": round(rt["ts_min"], 4),
         "dense_tflops": round(dense_tflops, 2),
         "torch_sdpa_ms": None if sdpa_ms is None else round(sdpa_ms, 4),
         "dense_speedup_vs_torch_sdpa": None if sdpa_ms is None else round(sdpa_ms / td, 3),
@@ -346,6 +409,7 @@ def main():
         # extra anchor work over a dense step, spread over the anchor's steps,
         # in units of the dense step (density-equivalent overhead)
         "anchor_overhead_ds": round((anchor_ms - td) / (cfg.n_reuse + 1) / td, 4),
+        "second_density": second,
         "roofline": roofline,
         "sparse_hbm": hbm,
         "cpu_baseline": cpu,

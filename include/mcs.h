@@ -46,8 +46,11 @@
  *
  * Device data is not validated (checking it would cost a pass over it):
  *   - perm must be a permutation of 0 .. n_pad-1 per head, as mcs_group
- *     writes it.  Its entries address query and output rows directly, so an
- *     entry outside 0 .. n_pad-1 makes a kernel read and write out of bounds.
+ *     writes it.  Its entries address query and output rows, but every
+ *     kernel range-checks them: an entry outside 0 .. n_pad-1 reads query row
+ *     0, counts as a padding row in the group scores and has no output row
+ *     written, so a corrupted perm gives wrong results, never an access
+ *     outside the tensors.
  *   - kv_idx entries must lie in 0 .. n_valid-1.  The K/V gathers are
  *     buffer loads bounded by the head's rows, so an entry outside that range
  *     reads a padding row, another row of the head or zeros, never memory
@@ -169,6 +172,10 @@ int32_t mcs_group_kmeans(const mcs_dims* dims, const uint16_t* q, int32_t iters,
  *   workspace: mcs_anchor_select_workspace_bytes(dims, topk) lets all heads
  *           run at once; any size >= mcs_anchor_select_min_workspace_bytes
  *           works (heads are then processed in chunks).
+ * When the workspace holds all heads, it keeps after the call the fp32 group
+ * scores the selection ranked, from its first byte on, as one row-major
+ * [batch*heads, n_pad/C, n_valid] array (for inspection and testing; with a
+ * smaller workspace only the last chunk of heads remains, at the start).
  */
 size_t mcs_anchor_select_workspace_bytes(const mcs_dims* dims, int32_t topk);
 size_t mcs_anchor_select_min_workspace_bytes(const mcs_dims* dims, int32_t topk);

@@ -30,7 +30,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmcs.so")
+# MCS_LIBRARY may name another build of the same library (e.g. the
+# sanitizer-instrumented one the build step makes with --sanitized)
+LIB_PATH = os.environ.get("MCS_LIBRARY") or os.path.join(_PKG, "libmcs.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mcs.h")
 
 MCS_OK, MCS_ERR_INVALID_ARG, MCS_ERR_UNSUPPORTED, MCS_ERR_WORKSPACE, MCS_ERR_HIP = range(5)
@@ -190,6 +192,18 @@ def group_workspace_bytes(dims: Dims) -> int:
 def anchor_select_workspace_bytes(dims: Dims, topk: int, minimum: bool = False) -> int:
     fn = lib().mcs_anchor_select_min_workspace_bytes if minimum else lib().mcs_anchor_select_workspace_bytes
     return int(fn(ctypes.byref(dims), topk))
+
+
+def anchor_scores(workspace: torch.Tensor, dims: Dims) -> torch.Tensor:
+    """The fp32 group scores [B*H, n_pad/C, n_valid] that mcs_anchor_select
+    left in an all-heads workspace (the layout include/mcs.h documents), as a
+    view of `workspace`."""
+    bh = dims.batch * dims.heads
+    G = dims.n_pad // dims.group_size
+    if workspace.numel() * workspace.element_size() < anchor_select_workspace_bytes(dims, 1):
+        raise ValueError("workspace does not hold the scores of all heads")
+    n = bh * G * dims.n_valid
+    return workspace.view(torch.uint8)[: 4 * n].view(torch.float32).view(bh, G, dims.n_valid)
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:

@@ -1,7 +1,13 @@
 """Build libmcs.so (the C-ABI library of the hot path) for gfx950 with hipcc.
 
-Usage: python -m sparse_attention_diffusion_attn_amd.build
+Usage: python -m sparse_attention_diffusion_attn_amd.build [--sanitized]
 Objects go to <package>/_build/, the library to <package>/libmcs.so.
+
+--sanitized also builds <package>/_build/libmcs_san.so: the same library with
+its host code (mcs_api.cpp: argument validation, layout and workspace
+arithmetic, launch set-up) compiled by the host compiler under
+AddressSanitizer and UndefinedBehaviorSanitizer, linked with the unchanged
+kernel objects.  Only host code is instrumented.
 """
 from __future__ import annotations
 
@@ -50,6 +56,37 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+SAN_OUT = os.path.join(PKG, "_build", "libmcs_san.so")
+GXX = os.environ.get("CXX_HOST", "g++")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libmcs_san.so: mcs_api.cpp under ASan + UBSan (host compiler), the
+    kernel objects of the last build() unchanged."""
+    bdir = os.path.join(PKG, "_build")
+    kernel_objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES if s.endswith(".hip")]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        build(verbose)
+    api_obj = os.path.join(bdir, "mcs_api_san.o")
+    cmd = [GXX, "-std=c++17", "-O1", "-g", "-fPIC", *SAN_FLAGS, "-D__HIP_PLATFORM_AMD__",
+           "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+           "-c", os.path.join(CSRC, "mcs_api.cpp"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host compile of mcs_api.cpp failed:\n{r.stderr}")
+    cmd = [GXX, "-shared", *SAN_FLAGS, "-o", SAN_OUT, api_obj, *kernel_objs,
+           "-L", "/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the sanitized library failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_OUT}")
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    if "--sanitized" in sys.argv[1:]:
+        build_sanitized(verbose=True)
     sys.exit(0)

@@ -66,8 +66,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const uint16_t* Vb = p.v + head_offset(p.sv, bh, p.heads);
 
   // ---- query rows of this lane (B operand of S^T, resident in VGPRs) ----
+  // A perm entry outside 0 .. n_pad-1 (perm is caller memory that may have
+  // travelled through the host) is never used as an address: such a lane
+  // reads row 0 and writes nothing.
   const int qpos = g * C + 32 * rb + ql;
-  const int qrow = (MODE == ATTN_DENSE) ? qpos : p.perm[(size_t)bh * p.n_pad + qpos];
+  const int qraw = (MODE == ATTN_DENSE) ? qpos : p.perm[(size_t)bh * p.n_pad + qpos];
+  const bool row_ok = (uint32_t)qraw < (uint32_t)p.n_pad;
+  const int qrow = row_ok ? qraw : 0;
   bf16x8 qreg[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
@@ -363,6 +368,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
         x[2] = bf16_to_f32(ov.y & 0xffff) - x[2];
         x[3] = bf16_to_f32(ov.y >> 16) - x[3];
       }
+      if (!row_ok) continue;
       uint2 st;
       if (valid) {
         st.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);

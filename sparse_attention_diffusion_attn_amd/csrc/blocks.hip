@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void meanpool_kernel(BlockParams p) {
   int cnt = 0;
   for (int r = pt; r < C; r += PARTS) {
     const int row = mem[r];
-    if (row < p.n_valid) {
+    if ((uint32_t)row < (uint32_t)p.n_valid) {  // padding rows and bad entries excluded
       s += (double)bf16_to_f32(Q[(int64_t)row * p.sq.n + d]);
       ++cnt;
     }

@@ -791,6 +791,8 @@ int32_t mcs_residual_counts(const mcs_dims* dims, const uint16_t* q, const uint1
   MCS_TRY(varlen_common(dims, q, k, v, perm, kv_idx, kv_stride, kv_count, scale));
   MCS_TRY(check_ptr(o_full, "o_full"));
   MCS_TRY(check_ptr(r, "r"));
+  if (r == q || r == k || r == v)
+    return fail(MCS_ERR_INVALID_ARG, "r must not alias q, k or v");
   MCS_TRY(attn_varlen(mcs::ATTN_RESID, dims, q, k, v, perm, kv_idx, kv_stride, kv_count, scale,
                       o_full, r, (hipStream_t)stream));
   return ok();

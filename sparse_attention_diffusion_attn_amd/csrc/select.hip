@@ -56,8 +56,11 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
   const uint16_t* Kb = p.k + head_offset(p.sk, bh, p.heads);
   const int32_t* permb = p.perm + (size_t)bh * p.n_pad + (size_t)g * C;
 
-  // A operand of S = Q K^T: this lane's query row 32rb + ql.
-  const int qrow = permb[32 * rb + ql];
+  // A operand of S = Q K^T: this lane's query row 32rb + ql.  A perm entry
+  // outside 0 .. n_pad-1 is never used as an address: its lane reads row 0,
+  // and below it counts as a padding row (no term in the scores).
+  const int qraw = permb[32 * rb + ql];
+  const int qrow = ((uint32_t)qraw < (uint32_t)p.n_pad) ? qraw : 0;
   bf16x8 qreg[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int r = permb[32 * rb + 8 * (j >> 2) + 4 * h + (j & 3)];
-    lse2[j] = (r < p.n_valid) ? p.lse[(size_t)bh * p.n_pad + r] * kLog2e : INFINITY;
+    lse2[j] = ((uint32_t)r < (uint32_t)p.n_valid) ? p.lse[(size_t)bh * p.n_pad + r] * kLog2e : INFINITY;
   }
 
   const int nk = p.n_valid;

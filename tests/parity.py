@@ -74,6 +74,74 @@ def check_selection(gpu_idx, a_row, k):
     return "band"
 
 
+def check_selection_exact(gpu_idx, gpu_scores_row, k):
+    """Index work on the same inputs: the GPU's kv_idx row must be exactly the
+    oracle's top-k (ties to the lower key index, ascending) of the fp32 scores
+    the GPU ranked (fp32 -> fp64 is exact, so the order is the same)."""
+    ref = orc.topk_select(np.asarray(gpu_scores_row, np.float64)[None], k)[0]
+    assert np.array_equal(np.asarray(gpu_idx, np.int64), ref), \
+        "selection differs from the top-k of the GPU's own scores"
+
+
+# fp32 error of the score pass, per term exp2(x) with
+#   x = fma(s, c2, -lse2),  s = q.k accumulated in fp32 from exact bf16
+#   products, c2 = fp32(fp32(scale) * fp32(log2 e)), lse2 = fp32(lse * log2 e),
+# against the fp64 value with the same (fp32) lse:
+#   |dx| <= c2 * d * 2^-23 * sum|q_e k_e|          (accumulation of d products,
+#                                                    2u per add for safety)
+#         + 2^-24 * (3 |s| c2 + |x| + 2 |lse| log2 e) (scale, fma, lse2 roundings)
+#   the term's relative error <= ln2 |dx| + 2^-22    (v_exp_f32, 4 ulp allowed)
+# then the sum of the group's C terms (16 in a lane, the other half-wave, the
+# wavefront partials: 20 adds deep) <= 40 * 2^-24 of the sum, and every term
+# may flush to zero below 2^-126.
+def score_error_bound(q_rows, k, lse_rows, scale, n_valid):
+    """Elementwise bound on |a_gpu - a| for one group (q_rows: its valid
+    members, lse_rows their fp32 lse as fp64; k: [n_valid, d])."""
+    q_rows = np.asarray(q_rows, np.float64)
+    k = np.asarray(k, np.float64)[:n_valid]
+    lse_rows = np.asarray(lse_rows, np.float64)
+    d = q_rows.shape[1]
+    log2e = 1.0 / np.log(2.0)
+    c2 = scale * log2e
+    s = q_rows @ k.T
+    sabs = np.abs(q_rows) @ np.abs(k).T
+    x = (scale * s - lse_rows[:, None]) * log2e
+    t = np.exp2(x)
+    dx = c2 * d * 2.0 ** -23 * sabs + 2.0 ** -24 * (3 * np.abs(s) * c2 + np.abs(x)
+                                                     + 2 * np.abs(lse_rows)[:, None] * log2e)
+    per_term = t * (np.log(2.0) * dx + 2.0 ** -22)
+    a = t.sum(axis=0)
+    return per_term.sum(axis=0) + 40 * 2.0 ** -24 * a + q_rows.shape[0] * 2.0 ** -126
+
+
+def check_scores(gpu_row, ref_row, bound_row):
+    """fp32 group scores against the oracle's (computed with the GPU's lse),
+    elementwise within score_error_bound.  Returns (max relative error, max
+    error / bound)."""
+    gpu_row = np.asarray(gpu_row, np.float64)
+    ref_row = np.asarray(ref_row, np.float64)
+    err = np.abs(gpu_row - ref_row)
+    bad = err > bound_row
+    assert not bad.any(), (f"{int(bad.sum())} scores outside the fp32 bound, worst key "
+                           f"{int(np.argmax(err / bound_row))}")
+    rel = float((err / np.maximum(ref_row, 1e-300)).max())
+    return rel, float((err / bound_row).max())
+
+
+def selection_stats(gpu_idx, a_row, k):
+    """Diagnostics of one group against the fp64 scores: the population of the
+    tie band [tau' - eps, tau + eps] and the fraction of the GPU set the fp64
+    top-k shares."""
+    a_row = np.asarray(a_row, np.float64)
+    srt = np.sort(a_row)[::-1]
+    tau = srt[k - 1]
+    tau_next = srt[k] if k < len(a_row) else -np.inf
+    band = int(((a_row >= tau_next - EPS_SEL) & (a_row <= tau + EPS_SEL)).sum())
+    ref = orc.topk_select(a_row[None], k)[0]
+    agree = np.intersect1d(np.asarray(gpu_idx), ref).size / k
+    return band, agree
+
+
 def check_block_selection(gpu_blocks, scores_row, n_b):
     """Compare one group's GPU block set with the oracle's block scores: equal
     outside a relative tie band, else every clearly better block present and no

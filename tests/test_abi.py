@@ -158,6 +158,13 @@ def test_counts_calls_checks():
     assert "o_full" in err()
     assert lib.mcs_sparse_attn_counts(b, P, P, P, P, P, 8, P, 0.1, None, P, None) == mcs.MCS_ERR_INVALID_ARG
     assert "alias" in err()
+    # R is written while the kernel reads K/V rows of other tokens: it may not
+    # alias q, k or v
+    q, k, v = P, P + 0x100000, P + 0x200000
+    for r in (q, k, v):
+        assert lib.mcs_residual_counts(b, q, k, v, P, P, 8, P, 0.1, P + 0x300000, r, None) == \
+            mcs.MCS_ERR_INVALID_ARG
+        assert "alias" in err()
 
 
 def _layout(fn, dm):
@@ -268,3 +275,4 @@ def test_kmeans_checks():
     assert lib.mcs_group_kmeans(b, P, 3, P, MIS, P, need, None) == mcs.MCS_ERR_INVALID_ARG
     assert lib.mcs_group_kmeans(b, P, 3, P, None, P, need - 1, None) == mcs.MCS_ERR_WORKSPACE
     assert lib.mcs_group_kmeans(b, P, 3, P, None, P + 16, need, None) == mcs.MCS_ERR_WORKSPACE
+

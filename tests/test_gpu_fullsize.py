@@ -4,6 +4,12 @@ sampled outputs: heads {0, H-1}, and in each the first group, the last group
 (which holds the padded tokens, if any) and six seeded random groups.  Grouping
 is checked level by level on those heads; every head's perm is checked to be a
 partition into ascending groups of C.
+
+Selection is checked twice per sampled group: bit-exact on the same inputs
+(kv_idx equals the oracle's top-k of the fp32 scores the GPU ranked, read back
+from the anchor workspace, whose scores must match the oracle's within the
+fp32 error bound of tests/parity.py), and against the fp64 oracle's own scores
+under the tie-band rule.
 """
 import functools
 
@@ -58,7 +64,10 @@ def test_fullsize_pipeline_sampled(mcs, name):
     nv, C, sc, G, H = cfg.n_valid, cfg.group_size, cfg.scale, cfg.groups, cfg.heads
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     perm = mcs.group(qd, nv, C, cfg.power_iters)
-    o_full, lse, kv = mcs.anchor_select(qd, kd, vd, perm, nv, C, cfg.topk, sc)
+    # an all-heads workspace keeps the fp32 scores the top-k ranked
+    dims = mcs.make_dims(1, H, nv, cfg.n_pad, cfg.head_dim, C)
+    ws = torch.empty(mcs.anchor_select_workspace_bytes(dims, cfg.topk), dtype=torch.uint8, device=DEV)
+    o_full, lse, kv = mcs.anchor_select(qd, kd, vd, perm, nv, C, cfg.topk, sc, workspace=ws)
     r = mcs.residual(qd, kd, vd, perm, kv, o_full, nv, C, sc)
     del qd, kd, vd
     o = mcs.sparse_attn(qt.to(DEV), kt.to(DEV), vt.to(DEV), perm, kv, r, nv, C, sc)
@@ -75,7 +84,9 @@ def test_fullsize_pipeline_sampled(mcs, name):
 
     groups = sd.sample_groups(cfg)
     rules = {"strict": 0, "band": 0}
+    worst_rel, worst_frac = 0.0, 0.0
     perm_h_all, kv_h_all = perm.cpu().numpy(), kv.cpu().numpy()
+    gpu_scores = mcs.anchor_scores(ws, dims)
     for h in (0, H - 1):
         f = par.bf16_to_f64
         qh, kh, vh = f(q[0, h]), f(k[0, h]), f(v[0, h])
@@ -83,13 +94,29 @@ def test_fullsize_pipeline_sampled(mcs, name):
         rows = np.concatenate([ph[g * C:(g + 1) * C] for g in groups])
         ref_o, ref_l = orc.dense_attention(qh, kh, vh, nv, sc, rows=rows)
         par.assert_close(f(o_full[0, h])[rows], ref_o, rows=rows < nv, what=f"{name} O_full h{h}")
-        lse_g = lse[0, h].double().cpu().numpy()[rows]
-        assert np.abs(lse_g - ref_l)[rows < nv].max() < 1e-3
+        lse_gpu = lse[0, h].double().cpu().numpy()
+        assert np.abs(lse_gpu[rows] - ref_l)[rows < nv].max() < 1e-3
         lse_full = np.zeros(cfg.n_pad)
         lse_full[rows] = ref_l
         a = orc.group_scores(qh, kh, ph, lse_full, nv, C, sc, groups=groups)
+        # the scores the GPU ranked, against the oracle's with the GPU's lse
+        a_gl = orc.group_scores(qh, kh, ph, lse_gpu, nv, C, sc, groups=groups)
         for i, g in enumerate(groups):
-            rules[par.check_selection(kvh[g], a[i], cfg.topk)] += 1
+            ga = gpu_scores[h, g].cpu().numpy()
+            mem = ph[g * C:(g + 1) * C]
+            mem = mem[mem < nv]
+            bound = par.score_error_bound(qh[mem], kh, lse_gpu[mem], sc, nv)
+            rel, frac = par.check_scores(ga, a_gl[i], bound)
+            worst_rel, worst_frac = max(worst_rel, rel), max(worst_frac, frac)
+            # index work bit-exact on the same inputs
+            par.check_selection_exact(kvh[g], ga, cfg.topk)
+            # and against the fp64 oracle's own scores (R5 rule)
+            rule = par.check_selection(kvh[g], a[i], cfg.topk)
+            rules[rule] += 1
+            band, agree = par.selection_stats(kvh[g], a[i], cfg.topk)
+            print(f"[{name}] h{h} g{g}: rule {rule}, tie band holds {band} keys, "
+                  f"{agree:.5f} of the set shared with the fp64 top-k, scores max rel err {rel:.2e}",
+                  flush=True)
         o_sp = orc.sparse_attention(qh, kh, vh, ph, kvh[groups], nv, C, sc, groups=groups)
         valid = rows < nv
         par.assert_close(f(r[0, h])[rows], (f(o_full[0, h]) - o_sp)[rows], rows=valid, what=f"{name} R h{h}")
@@ -97,7 +124,9 @@ def test_fullsize_pipeline_sampled(mcs, name):
                              groups=groups)
         par.assert_close(f(o[0, h])[rows], ref[rows], rows=valid, what=f"{name} reuse O h{h}")
         assert np.all(f(o[0, h])[rows[~valid]] == 0)
-    print(f"[{name}] selection rules on sampled groups: {rules}", flush=True)
+    print(f"[{name}] selection rules on sampled groups: {rules}; kv_idx equal to the top-k of the GPU's "
+          f"scores in all {sum(rules.values())}; scores max rel err {worst_rel:.2e}, "
+          f"max err / bound {worst_frac:.3f}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["480p", "3d", "hunyuan720p_15"])

@@ -100,13 +100,20 @@ def test_dense_attn(mcs, shape):
         assert np.all(l[nv:] == 0) and np.all(f64(o[0, h])[nv:] == 0)
 
 
-def run_anchor(mcs, cfg, q, k, v):
+def run_anchor(mcs, cfg, q, k, v, ws=None):
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     perm = mcs.group(qd, cfg.n_valid, cfg.group_size, cfg.power_iters)
-    o_full, lse, kv = mcs.anchor_select(qd, kd, vd, perm, cfg.n_valid, cfg.group_size, cfg.topk, cfg.scale)
+    o_full, lse, kv = mcs.anchor_select(qd, kd, vd, perm, cfg.n_valid, cfg.group_size, cfg.topk, cfg.scale,
+                                        workspace=ws)
     r = mcs.residual(qd, kd, vd, perm, kv, o_full, cfg.n_valid, cfg.group_size, cfg.scale)
     torch.cuda.synchronize()
     return perm, o_full, lse, kv, r
+
+
+def all_heads_ws(mcs, cfg, topk=None):
+    dims = mcs.make_dims(cfg.batch, cfg.heads, cfg.n_valid, cfg.n_pad, cfg.head_dim, cfg.group_size)
+    nbytes = mcs.anchor_select_workspace_bytes(dims, cfg.topk if topk is None else topk)
+    return dims, torch.empty(nbytes, dtype=torch.uint8, device=DEV)
 
 
 TINY_LIKE = [
@@ -121,9 +128,11 @@ TINY_LIKE = [
 def test_anchor_and_reuse_pipeline(mcs, cfg):
     steps = sd.generate(cfg)
     q, k, v = steps[0]
-    perm, o_full, lse, kv, r = run_anchor(mcs, cfg, q, k, v)
+    dims, ws = all_heads_ws(mcs, cfg)
+    perm, o_full, lse, kv, r = run_anchor(mcs, cfg, q, k, v, ws)
     nv, C, sc, G = cfg.n_valid, cfg.group_size, cfg.scale, cfg.groups
     perm_h, kv_h = perm.cpu().numpy(), kv.cpu().numpy()
+    gpu_scores = mcs.anchor_scores(ws, dims).cpu().numpy()
     rules = {"strict": 0, "band": 0}
     for h in range(cfg.heads):
         qh, kh, vh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
@@ -136,9 +145,19 @@ def test_anchor_and_reuse_pipeline(mcs, cfg):
         ref_o, ref_l = orc.dense_attention(qh, kh, vh, nv, sc)
         par.assert_close(f64(o_full[0, h])[:nv], ref_o[:nv], what="O_full")
         assert np.abs(lse[0, h].double().cpu().numpy()[:nv] - ref_l[:nv]).max() < 1e-3
-        # pass 2 + top-k, with the GPU's groups
+        # pass 2 + top-k, with the GPU's groups: the GPU's fp32 scores within
+        # their error bound of the oracle's (with the GPU's lse), the index
+        # sets bit-exact against the top-k of those scores, and within the
+        # tie-band rule against the fp64 oracle's own scores
         a = orc.group_scores(qh, kh, p, ref_l, nv, C, sc)
+        lse_gpu = lse[0, h].double().cpu().numpy()
+        a_gl = orc.group_scores(qh, kh, p, lse_gpu, nv, C, sc)
+        bh = h  # batch 1
         for g in range(G):
+            mem = p[g * C:(g + 1) * C]
+            mem = mem[mem < nv]
+            par.check_scores(gpu_scores[bh, g], a_gl[g], par.score_error_bound(qh[mem], kh, lse_gpu[mem], sc, nv))
+            par.check_selection_exact(kv_h[0, h, g], gpu_scores[bh, g], cfg.topk)
             rules[par.check_selection(kv_h[0, h, g], a[g], cfg.topk)] += 1
         # residual, isolated: the GPU's O_full as input
         o_sp = orc.sparse_attention(qh, kh, vh, p, kv_h[0, h], nv, C, sc)
@@ -199,3 +218,45 @@ def test_small_workspace_head_chunks(mcs):
     o2, l2, kv2 = mcs.anchor_select(qd, kd, vd, perm, cfg.n_valid, 64, cfg.topk, cfg.scale, workspace=small)
     torch.cuda.synchronize()
     assert torch.equal(kv1, kv2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("d,C,topk", [(64, 64, 2501), (128, 128, 2403)])
+def test_topk_planted_ties_long_rows(mcs, d, C, topk):
+    """Rows of 10000 keys (the top-k's histogram passes take their eight-loads-
+    in-flight loop twice, then the tail) in which every key row occurs four
+    times, so every score is tied four ways and the k-th score's tie run is
+    split (topk = 4m + 1 or 4m + 3): the selection must be exactly the top-k of
+    the GPU's own scores, ties to the lower key index."""
+    nv = 10000
+    cfg = sd.custom("ties", heads=1, n_valid=nv, head_dim=d, group_size=C, density_pct=25, n_clusters=8)
+    q, k, v = sd.generate(cfg, steps=1)[0]
+    base = nv // 4
+    k[0, 0, base:nv] = k[0, 0, :base].repeat(3, 1)
+    dims, ws = all_heads_ws(mcs, cfg, topk)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    perm = mcs.group(qd, nv, C, cfg.power_iters)
+    o_full, lse, kv = mcs.anchor_select(qd, kd, vd, perm, nv, C, topk, cfg.scale, workspace=ws)
+    torch.cuda.synchronize()
+    sc_gpu = mcs.anchor_scores(ws, dims)[0].cpu().numpy()
+    kvh, p = kv[0, 0].cpu().numpy(), perm[0, 0].cpu().numpy()
+    # identical key rows got bitwise identical scores
+    j = np.arange(nv)
+    assert np.array_equal(sc_gpu[:, j], sc_gpu[:, j % base])
+    split = 0
+    qh, kh = f64(q[0, 0]), f64(k[0, 0])
+    lse_gpu = lse[0, 0].double().cpu().numpy()
+    for g in range(cfg.groups):
+        row = sc_gpu[g]
+        par.check_selection_exact(kvh[g], row, topk)
+        tau = np.sort(row)[::-1][topk - 1]
+        n_eq, n_sel = int((row == tau).sum()), int((row[kvh[g]] == tau).sum())
+        assert n_eq >= 4 and 0 < n_sel <= n_eq
+        split += n_sel < n_eq
+    assert split > cfg.groups // 2, "the k-th score's tie run was rarely split"
+    # the scores themselves, on a few groups
+    for g in (0, cfg.groups // 2, cfg.groups - 1):
+        mem = p[g * C:(g + 1) * C]
+        mem = mem[mem < nv]
+        a_gl = orc.group_scores(qh, kh, p, lse_gpu, nv, C, cfg.scale, groups=[g])[0]
+        par.check_scores(sc_gpu[g], a_gl, par.score_error_bound(qh[mem], kh, lse_gpu[mem], cfg.scale, nv))
+    print(f"ties d{d} C{C} k{topk}: tie run split at the k-th score in {split} of {cfg.groups} groups")
