@@ -185,6 +185,27 @@ int32_t mcs_anchor_select(const mcs_dims* dims, const uint16_t* q, const uint16_
                           size_t workspace_bytes, void* stream);
 
 /*
+ * mcs_anchor_select_noalloc — mcs_anchor_select for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and results as
+ * mcs_anchor_select without the workspace: the scores live in a fixed
+ * MCS_NOALLOC_SCRATCH_BYTES array that the library's device code holds on
+ * every GPU it runs on until the process ends; heads are processed in chunks
+ * of as many as fit.  Shapes whose single head needs more than that
+ * (mcs_anchor_select_min_workspace_bytes > MCS_NOALLOC_SCRATCH_BYTES) are
+ * rejected with MCS_ERR_UNSUPPORTED.  The call allocates nothing; its first
+ * call on a device looks up that device's array address (the device must be
+ * current and `stream` must belong to it).  All calls on one GPU share the
+ * array: calls whose work overlaps on one GPU (other streams, unordered host
+ * threads) race; calls ordered on one stream do not.
+ */
+#define MCS_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+int32_t mcs_anchor_select_noalloc(const mcs_dims* dims, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const int32_t* perm, int32_t topk,
+                                  float scale, uint16_t* o_full, float* lse, int32_t* kv_idx,
+                                  void* stream);
+
+/*
  * mcs_residual — R = O_full - SparseAttn(Q, K, V; perm, kv_idx) at the anchor
  * (onedev.kr summary, "what is different").  The sparse softmax is normalised
  * over each group's own index set.  Padded rows of R are 0.

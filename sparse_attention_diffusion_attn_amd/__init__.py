@@ -75,6 +75,7 @@ _SIGNATURES = {
     "mcs_anchor_select_workspace_bytes": (_SZ, [_DP, _I]),
     "mcs_anchor_select_min_workspace_bytes": (_SZ, [_DP, _I]),
     "mcs_anchor_select": (_I, [_DP, _P, _P, _P, _P, _I, _F, _P, _P, _P, _P, _SZ, _P]),
+    "mcs_anchor_select_noalloc": (_I, [_DP, _P, _P, _P, _P, _I, _F, _P, _P, _P, _P]),
     "mcs_residual": (_I, [_DP, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P]),
     "mcs_sparse_attn": (_I, [_DP, _P, _P, _P, _P, _P, _I, _F, _P, _P, _P]),
     "mcs_dense_attn": (_I, [_DP, _P, _P, _P, _F, _P, _P, _P]),
@@ -292,6 +293,34 @@ def anchor_select(q, k, v, perm, n_valid: int, group_size: int, topk: int,
         st = lib().mcs_anchor_select_strided(ctypes.byref(dims), ctypes.byref(lay), *args)
     _check(st, "mcs_anchor_select")
     return o_full, lse, kv_idx
+
+
+def anchor_select_noalloc(q, k, v, perm, n_valid: int, group_size: int, topk: int,
+                          scale: Optional[float] = None, o_full=None, lse=None, kv_idx=None,
+                          stream=None):
+    """mcs_anchor_select with the library's fixed device scratch as workspace
+    (mcs_anchor_select_noalloc): nothing is allocated beyond the outputs
+    (pass them in to allocate nothing at all).  Contiguous tensors only."""
+    dims = _dims_of(q, n_valid, group_size)
+    b, h, n_pad, d = q.shape
+    G = n_pad // group_size
+    scale = default_scale(d) if scale is None else scale
+    if o_full is None:
+        o_full = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((b, h, n_pad), dtype=torch.float32, device=q.device)
+    if kv_idx is None:
+        kv_idx = torch.empty((b, h, G, topk), dtype=torch.int32, device=q.device)
+    st = lib().mcs_anchor_select_noalloc(
+        ctypes.byref(dims), _need(q, "q", torch.bfloat16, q.shape), _need(k, "k", torch.bfloat16, q.shape),
+        _need(v, "v", torch.bfloat16, q.shape), _need(perm, "perm", torch.int32, (b, h, n_pad)), topk, scale,
+        _need(o_full, "o_full", torch.bfloat16, q.shape), _need(lse, "lse", torch.float32, (b, h, n_pad)),
+        _need(kv_idx, "kv_idx", torch.int32, (b, h, G, topk)), _stream(stream))
+    _check(st, "mcs_anchor_select_noalloc")
+    return o_full, lse, kv_idx
+
+
+NOALLOC_SCRATCH_BYTES = 192 << 20
 
 
 def residual(q, k, v, perm, kv_idx, o_full, n_valid: int, group_size: int,

@@ -32,6 +32,14 @@ int32_t ok() {
   return MCS_OK;
 }
 
+}  // namespace
+
+namespace mcs {
+int32_t api_fail(int32_t code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace mcs
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

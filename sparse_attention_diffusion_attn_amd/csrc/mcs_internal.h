@@ -128,6 +128,9 @@ struct KmeansParams {
   int32_t heads, n_pad, groups, tiles, label_bits;
 };
 
+// Records `msg` as this thread's last error (mcs_last_error) and returns code.
+int32_t api_fail(int32_t code, const char* msg);
+
 hipError_t launch_attention(int mode, int head_dim, int group_size, const AttnParams& p,
                             hipStream_t s);
 hipError_t launch_scores(int head_dim, int group_size, const ScoreParams& p, hipStream_t s);

@@ -276,3 +276,20 @@ def test_kmeans_checks():
     assert lib.mcs_group_kmeans(b, P, 3, P, None, P, need - 1, None) == mcs.MCS_ERR_WORKSPACE
     assert lib.mcs_group_kmeans(b, P, 3, P, None, P + 16, need, None) == mcs.MCS_ERR_WORKSPACE
 
+
+def test_noalloc_validation_before_any_gpu_work():
+    """mcs_anchor_select_noalloc rejects, on the host, shapes whose single head
+    needs more than the fixed scratch, and bad shapes as mcs_anchor_select does."""
+    lib = mcs.lib()
+    hy = d(heads=1, n_valid=118800, n_pad=118912)
+    need = lib.mcs_anchor_select_min_workspace_bytes(ctypes.byref(hy), 29700)
+    assert need > mcs.NOALLOC_SCRATCH_BYTES
+    assert lib.mcs_anchor_select_noalloc(ctypes.byref(hy), P, P, P, P, 29700, 0.1, P, P, P, None) == \
+        mcs.MCS_ERR_UNSUPPORTED
+    assert "scratch" in err()
+    assert lib.mcs_anchor_select_noalloc(ctypes.byref(d(head_dim=80)), P, P, P, P, 10, 0.1, P, P, P, None) == \
+        mcs.MCS_ERR_UNSUPPORTED
+    assert "head_dim" in err()
+    assert lib.mcs_anchor_select_noalloc(ctypes.byref(d()), P, P, P, P, 0, 0.1, P, P, P, None) == \
+        mcs.MCS_ERR_INVALID_ARG
+    assert "topk" in err()
