@@ -197,36 +197,41 @@ int32_t resolve_layout(const mcs_dims* d, const mcs_layout* l, Lay* out) {
 }
 
 // ---- workspace layouts ----
-// Depths whose largest node holds at least gram_min(d) groups run the power
-// iteration on the node's covariance (Gram path); the others on the rows.
-// With d = 128 the covariance takes 128 KiB of LDS per node, one node per CU,
-// which loses to the row passes once nodes are small (measured: best from 4
-// groups up); with d = 64 (32 KiB) it wins down to 2-group nodes.
-int gram_min(int head_dim) { return head_dim == 64 ? 2 : 4; }
+// With power iterations, every depth runs the covariance path: entries of
+// the formed nodes (the root, then the left children of nodes of >= 3 groups)
+// as chunk partials, and the entries of every depth's nodes of >= 3 groups
+// kept for the next depth (two buffers, previous and current).
+size_t gram_entry_doubles(int head_dim) {
+  const size_t dt = (size_t)head_dim / 16;
+  return dt * (dt + 1) / 2 * 256 + (size_t)head_dim;
+}
 
-int gram_largest_node(int groups, int level) {  // ceil(G / 2^level)
+int largest_node(int groups, int level) {  // ceil(G / 2^level)
   return (int)(((int64_t)groups + ((int64_t)1 << level) - 1) >> level);
 }
-bool gram_level(int groups, int level, int head_dim) {
-  return gram_largest_node(groups, level) >= gram_min(head_dim);
-}
+
+// chunks of GRAM_CH blocks of the largest node formed at `level`
 int gram_chunks(int groups, int level) {
-  return (gram_largest_node(groups, level) + mcs::GRAM_CH - 1) / mcs::GRAM_CH;
+  const int m = (level == 0) ? groups : largest_node(groups, level - 1) / 2;
+  return (m + mcs::GRAM_CH - 1) / mcs::GRAM_CH;
 }
 
 struct GroupWs {
-  size_t partial, mu, vec, proj, perm, gram, total;
+  size_t partial, mu, vec, proj, perm, gram, gnode0, gnode1, total;
 };
 
 GroupWs group_ws(const mcs_dims* d) {
   const size_t bh = (size_t)d->batch * d->heads;
   const size_t G = (size_t)(d->n_pad / d->group_size);
-  const size_t dt = (size_t)d->head_dim / 16;
-  const size_t tile_doubles = dt * (dt + 1) / 2 * 256;
-  size_t gram = 0;  // chunk partials of the largest Gram depth
-  for (int l = 0; l < levels_for((int)G); ++l)
-    if (gram_level((int)G, l, d->head_dim))
-      gram = std::max(gram, ((size_t)1 << l) * (size_t)gram_chunks((int)G, l) * tile_doubles);
+  const size_t e = gram_entry_doubles(d->head_dim);
+  const int L = levels_for((int)G);
+  size_t gram = 0;  // chunk partials, largest depth
+  for (int l = 0; l < L; ++l) {
+    const size_t pslots = l == 0 ? 1 : (size_t)1 << (l - 1);
+    gram = std::max(gram, pslots * (size_t)gram_chunks((int)G, l) * e);
+  }
+  // entries kept at depth l <= L-2 (read at depth l+1)
+  const size_t gnode = L >= 2 ? ((size_t)1 << (L - 2)) * e : 0;
   GroupWs w;
   size_t o = 0;
   w.partial = o; o = align256(o + bh * G * d->head_dim * sizeof(double));
@@ -235,6 +240,8 @@ GroupWs group_ws(const mcs_dims* d) {
   w.proj = o;    o = align256(o + bh * (size_t)d->n_pad * sizeof(double));
   w.perm = o;    o = align256(o + bh * (size_t)d->n_pad * sizeof(int32_t));
   w.gram = o;    o = align256(o + bh * gram * sizeof(double));
+  w.gnode0 = o;  o = align256(o + bh * gnode * sizeof(double));
+  w.gnode1 = o;  o = align256(o + bh * gnode * sizeof(double));
   w.total = o;
   return w;
 }
@@ -406,6 +413,7 @@ int32_t mcs_group_strided(const mcs_dims* dims, const mcs_layout* layout, const 
   p.vec = (double*)(ws + w.vec);
   p.proj = (double*)(ws + w.proj);
   p.gram = (double*)(ws + w.gram);
+  double* gnode[2] = {(double*)(ws + w.gnode0), (double*)(ws + w.gnode1)};
   p.power_iters = power_iters;
   p.sq = lay.q;
   p.bh = (int64_t)dims->batch * dims->heads;
@@ -420,20 +428,20 @@ int32_t mcs_group_strided(const mcs_dims* dims, const mcs_layout* layout, const 
     p.level = lv;
     p.perm_cur = bufs[cur];
     p.perm_next = bufs[1 - cur];
-    MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 0, p, s), "pddp mean"));
-    MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 0, p, s), "pddp mean reduce"));
-    if (power_iters > 0 && gram_level(G, lv, d)) {
+    if (power_iters > 0) {
+      // covariance path: entries of the formed nodes, then per node its
+      // mean, centred matrix, power iterations and sign rule
       p.nch = gram_chunks(G, lv);
+      p.gram_store = (lv + 1 < L) ? 1 : 0;
+      p.gnode_prev = gnode[lv & 1];
+      p.gnode_cur = gnode[(lv + 1) & 1];
       MCS_TRY(hip_status(mcs::launch_pddp_gram(d, c, p, s), "pddp covariance"));
       MCS_TRY(hip_status(mcs::launch_pddp_gram_power(d, c, p, s), "pddp covariance power"));
     } else {
-      for (int it = 0; it < power_iters; ++it) {
-        p.fix_sign = (it == power_iters - 1) ? 1 : 0;
-        MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 1, p, s), "pddp power step"));
-        MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 1, p, s), "pddp power reduce"));
-      }
+      // no iterations: v stays v0; only the node means are needed
+      MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 0, p, s), "pddp mean"));
+      MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 0, p, s), "pddp mean reduce"));
     }
-    p.fix_sign = 0;
     MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 2, p, s), "pddp projection"));
     MCS_TRY(hip_status(mcs::launch_pddp_split(c, p, s), "pddp split"));
     cur = 1 - cur;

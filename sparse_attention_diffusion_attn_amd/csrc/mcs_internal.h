@@ -104,9 +104,14 @@ struct PddpParams {
   int32_t heads;
   int32_t n_pad, groups, level;
   int32_t fix_sign;       // reduce stage 1: apply the sign rule to v (last power step)
-  double* gram;           // Gram path: chunk partials [BH, 2^level, nch, tiles, 256]
-  int32_t nch;            // Gram path: chunks per node slot at this depth
-  int32_t power_iters;    // Gram path: power iterations
+  // covariance path; an entry is the upper 16x16 tiles of X^T X then the d
+  // row sums (gram_entry doubles)
+  double* gram;           // chunk partials of the formed nodes [BH, parent slots, nch, entry]
+  double* gnode_prev;     // entries of the previous depth's nodes [BH, 2^(level-1), entry]
+  double* gnode_cur;      // entries of this depth's nodes kept for the next [BH, 2^level, entry]
+  int32_t gram_store;     // keep this depth's entries (nodes of >= 3 groups) in gnode_cur
+  int32_t nch;            // chunks of GRAM_CH blocks of the largest formed node at this depth
+  int32_t power_iters;    // power iterations
 };
 
 // Blocks (of C rows) per work item of the Gram path.
@@ -149,9 +154,11 @@ hipError_t launch_pddp_partial(int head_dim, int group_size, int stage, const Pd
 hipError_t launch_pddp_reduce(int head_dim, int group_size, int stage, const PddpParams& p,
                               hipStream_t s);
 hipError_t launch_pddp_split(int group_size, const PddpParams& p, hipStream_t s);
-// Gram path of a depth: chunk partials of X^T X (launch_pddp_gram), then
-// (launch_pddp_gram_power) their sum per node and, per node, the centred
-// matrix, the power iterations and the sign rule (writes v)
+// Covariance path of a depth: X^T X and the row sums of the formed nodes (the
+// root, else the left children), chunk partials summed per node
+// (launch_pddp_gram); then per node its entry (right children: parent minus
+// left sibling), mean, centred matrix, power iterations and sign rule
+// (launch_pddp_gram_power, writes mu and v)
 hipError_t launch_pddp_gram(int head_dim, int group_size, const PddpParams& p, hipStream_t s);
 hipError_t launch_pddp_gram_power(int head_dim, int group_size, const PddpParams& p, hipStream_t s);
 

@@ -566,20 +566,32 @@ __global__ __launch_bounds__(512) void pddp_split_kernel(PddpParams p) {
   }
 }
 
-// ---- Gram path for the upper depths ----
-// At a depth whose nodes hold many groups, the power iteration runs on the
-// node's centred covariance instead of on its rows:
+// ---- covariance path ----
+// The power iteration runs on each node's centred covariance instead of on its
+// rows:
 //   Sigma = X^T X - n mu mu^T   (fp64, d x d, n = m*C rows, padding rows included)
-// which is the same operator v -> sum_r ((x_r - mu) . v)(x_r - mu), formed with
-// one pass over the rows on the fp64 matrix cores; the 20 iterations then cost
-// d^2 work per node instead of a pass over its rows each.
+// which is the same operator v -> sum_r ((x_r - mu) . v)(x_r - mu); the 20
+// iterations then cost d^2 work per node instead of a pass over its rows each.
+// X^T X and the row sum X^T 1 are additive over rows, so below the root only
+// one child of every split is formed from its rows (the left one, the first
+// floor(m/2) groups of the parent's segment, never larger than its sibling)
+// and the other is the parent's minus it; the node mean comes from the row
+// sum, so no separate mean pass is needed.
 //
-// pddp_gram_kernel: one workgroup per (head, node slot, chunk of GRAM_CH
-// blocks); X^T X of the chunk's rows with v_mfma_f64_16x16x4_f64, only the
-// upper-triangular 16x16 tiles (I <= J), written as a partial per chunk.
-// pddp_gram_power_kernel: one workgroup per node; sums the node's chunk
-// partials in chunk order, centres, runs the power iterations (v0 = 1/sqrt(d),
-// v kept when |Sigma v| = 0) and applies the sign rule, as the row path does.
+// A node's entry holds the upper-triangular 16 x 16 tiles of X^T X (I <= J,
+// row-major inside a tile, tiles in row-major upper order) followed by the d
+// row sums: GRAM_ENTRY(d) doubles.
+//
+// pddp_gram_kernel: one workgroup per (head, parent slot, chunk of GRAM_CH
+// blocks of the left child; the root itself at depth 0); X^T X of the chunk's
+// rows on v_mfma_f64_16x16x4_f64 and the row sums, written as a partial.
+// pddp_gram_sum_kernel: the chunk partials of each left child summed in chunk
+// order (depths whose left children span several chunks).
+// pddp_gram_power_kernel: one workgroup per node; its entry (left child or
+// root: the sum just formed; right child: parent entry minus left entry),
+// kept for the next depth when the node will split again; the mean, the
+// centred matrix held in registers, the power iterations (v0 = 1/sqrt(d), v
+// kept when |Sigma v| = 0) and the sign rule.
 
 template <int DT>
 __host__ __device__ constexpr int gram_tile_i(int t) {
@@ -600,6 +612,11 @@ __host__ __device__ constexpr int gram_tile_j(int t) {
     --len;
   }
   return i + t;
+}
+// index of upper tile (I, J), I <= J, in row-major upper order
+template <int DT>
+__host__ __device__ constexpr int gram_tile_index(int I, int J) {
+  return I * DT - (I * (I - 1)) / 2 + (J - I);
 }
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -637,6 +654,11 @@ __device__ __forceinline__ void gram_stores(double* dst, const f64x4 (&acc)[size
   (gram_store<DT, W, K>(dst, acc[K], lane), ...);
 }
 
+template <int D>
+__host__ __device__ constexpr int gram_entry() {
+  return (D / 16) * (D / 16 + 1) / 2 * 256 + D;
+}
+
 template <int D, int C, int W>
 __device__ __forceinline__ void gram_body(const PddpParams& p, char (*rows)[64 * (2 * D + 32)],
                                           const int32_t* pc, const uint16_t* Qb, int nrows,
@@ -650,6 +672,9 @@ __device__ __forceinline__ void gram_body(const PddpParams& p, char (*rows)[64 *
   f64x4 acc[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) acc[k] = (f64x4){0.0, 0.0, 0.0, 0.0};
+  double sx[DT];  // wave 0: row sums of dimensions 16*blk + lane % 16, rows lane/16 + 4 st
+#pragma unroll
+  for (int blk = 0; blk < DT; ++blk) sx[blk] = 0.0;
   uint4 nx[LPT];
 #pragma unroll
   for (int q = 0; q < LPT; ++q) {
@@ -683,6 +708,10 @@ __device__ __forceinline__ void gram_body(const PddpParams& p, char (*rows)[64 *
 #pragma unroll
       for (int blk = 0; blk < DT; ++blk) xv[blk] = (double)bf16_to_f32(xr[16 * blk]);
       gram_mfmas<DT, W>(xv, acc, std::make_integer_sequence<int, TPW>{});
+      if constexpr (W == 0) {
+#pragma unroll
+        for (int blk = 0; blk < DT; ++blk) sx[blk] += xv[blk];
+      }
     }
 #pragma unroll
     for (int q = 0; q < LPT; ++q) {
@@ -692,27 +721,53 @@ __device__ __forceinline__ void gram_body(const PddpParams& p, char (*rows)[64 *
     __syncthreads();
   }
   gram_stores<DT, W>(dst, acc, lane, std::make_integer_sequence<int, TPW>{});
+  if constexpr (W == 0) {
+    // the four row lanes of each dimension (l, l^16, l^32, l^48), fixed order
+#pragma unroll
+    for (int blk = 0; blk < DT; ++blk) {
+      const double x = add_xor32(add_xor16(sx[blk]));
+      if (lane < 16) dst[NT * 256 + 16 * blk + lane] = x;
+    }
+  }
+}
+
+// Slots of the nodes whose left children are formed at `level` (1 at the
+// root depth, else the parent depth's 2^(level-1)).
+__device__ __forceinline__ int gram_parent_slots(int level) { return level == 0 ? 1 : 1 << (level - 1); }
+
+// Rows formed for parent slot ps at `level`: the root (level 0), else the
+// left child of a parent of m >= 3 groups (m = 2 splits into two leaves,
+// which need no covariance).  Returns false if there is nothing to form.
+__device__ __forceinline__ bool gram_formed_node(int G, int level, int ps, int& s, int& m) {
+  if (level == 0) {
+    s = 0;
+    m = G;
+    return m >= 2;
+  }
+  if (!node_of_slot(G, level - 1, ps, s, m) || m < 3) return false;
+  m >>= 1;
+  return true;
 }
 
 template <int D, int C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void pddp_gram_kernel(
     PddpParams p) {
-  constexpr int DT = D / 16, NT = DT * (DT + 1) / 2;
+  constexpr int E = gram_entry<D>();
   __shared__ __attribute__((aligned(16))) char rows[2][64 * (2 * D + 32)];
   const int G = p.groups;
-  const int slots = 1 << p.level;
-  const int per_bh = slots * p.nch;
+  const int pslots = gram_parent_slots(p.level);
+  const int per_bh = pslots * p.nch;
   const int bh = blockIdx.x / per_bh;
   const int rem = blockIdx.x - bh * per_bh;
-  const int slot = rem / p.nch, j = rem - slot * p.nch;
+  const int ps = rem / p.nch, j = rem - ps * p.nch;
   int s, m;
-  if (!node_of_slot(G, p.level, slot, s, m) || m < 2) return;
+  if (!gram_formed_node(G, p.level, ps, s, m)) return;
   const int b0 = j * GRAM_CH;
   if (b0 >= m) return;
   const int nrows = (min(b0 + GRAM_CH, m) - b0) * C;
   const int32_t* pc = p.perm_cur + (int64_t)bh * p.n_pad + (int64_t)(s + b0) * C;
   const uint16_t* Qb = p.q + head_offset(p.sq, bh, p.heads);
-  double* dst = p.gram + ((int64_t)(bh * slots + slot) * p.nch + j) * (NT * 256);
+  double* dst = p.gram + ((int64_t)(bh * pslots + ps) * p.nch + j) * E;
   switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
     case 0: gram_body<D, C, 0>(p, rows, pc, Qb, nrows, dst); break;
     case 1: gram_body<D, C, 1>(p, rows, pc, Qb, nrows, dst); break;
@@ -721,44 +776,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
-// Sum of a node's chunk partials, in chunk order, written over chunk 0 (one
-// workgroup per (head, node slot, tile); each thread owns one tile entry, so
-// reading every chunk's value and then writing chunk 0's is safe in place).
+// Sum of a formed node's chunk partials, in chunk order, written over chunk 0
+// (one workgroup per (head, parent slot, segment): a segment is one tile of
+// 256 entries or the d row sums; each thread owns one entry, so reading every
+// chunk's value and then writing chunk 0's is safe in place).
 template <int D>
 __global__ __launch_bounds__(256) void pddp_gram_sum_kernel(PddpParams p) {
-  constexpr int DT = D / 16, NT = DT * (DT + 1) / 2;
+  constexpr int DT = D / 16, NT = DT * (DT + 1) / 2, E = gram_entry<D>();
   const int G = p.groups;
-  const int slots = 1 << p.level;
-  const int per_bh = slots * NT;
+  const int pslots = gram_parent_slots(p.level);
+  const int per_bh = pslots * (NT + 1);
   const int bh = blockIdx.x / per_bh;
   const int rem = blockIdx.x - bh * per_bh;
-  const int slot = rem / NT, t = rem - slot * NT;
+  const int ps = rem / (NT + 1), seg = rem - ps * (NT + 1);
   int s, m;
-  if (!node_of_slot(G, p.level, slot, s, m) || m < 2) return;
+  if (!gram_formed_node(G, p.level, ps, s, m)) return;
   const int nck = (m + GRAM_CH - 1) / GRAM_CH;
-  if (nck < 2) return;
-  double* src = p.gram + (int64_t)(bh * slots + slot) * p.nch * (NT * 256) + t * 256 + threadIdx.x;
+  if (nck < 2 || (int)threadIdx.x >= (seg < NT ? 256 : D)) return;
+  double* src = p.gram + (int64_t)(bh * pslots + ps) * p.nch * E + seg * 256 + threadIdx.x;
   double a = 0.0;
   int k = 0;
   for (; k + 8 <= nck; k += 8) {
     double v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(k + u) * (NT * 256)];
+    for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(k + u) * E];
 #pragma unroll
     for (int u = 0; u < 8; ++u) a += v[u];
   }
-  for (; k < nck; ++k) a += src[(int64_t)k * (NT * 256)];
+  for (; k < nck; ++k) a += src[(int64_t)k * E];
   src[0] = a;
 }
 
+// One workgroup of 256 threads per node.  Thread (i, part), i = t % D, part =
+// t / D, holds row i, columns part*D/PARTS .. +D/PARTS-1 of the centred
+// matrix in registers (64 values for d = 128, 16 for d = 64), so the kernel
+// needs almost no LDS and several nodes share a CU.  One step: each thread's
+// partial dot product with v (four interleaved accumulators, v read from LDS
+// as a broadcast), the PARTS partials of row i summed in part order, |w|^2
+// summed over the wavefronts of part 0, v = w / |w|.
 template <int D, int C>
 __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
-  constexpr int DT = D / 16, NT = DT * (DT + 1) / 2;
-  __shared__ double sig[D * D];
+  constexpr int DT = D / 16, NT = DT * (DT + 1) / 2, E = gram_entry<D>();
+  constexpr int PARTS = 256 / D, CW = D / PARTS, NWD = D / 64;
+  static_assert(CW % 4 == 0, "columns per thread");
   __shared__ double vec[D];
   __shared__ double mus[D];
-  __shared__ double red[2];
-  __shared__ double half[64];
+  __shared__ double red[PARTS][D];
+  __shared__ double nrm[NWD];
   __shared__ double vmag[D];
   __shared__ int vidx[D];
   const int G = p.groups;
@@ -767,56 +831,87 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   const int slot = blockIdx.x - bh * slots;
   int s, m;
   if (!node_of_slot(G, p.level, slot, s, m) || m < 2) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  // X^T X of the node (the chunk sums are already in chunk 0), centred and
-  // mirrored to a full matrix.  Pass k handles upper tile k (256 elements, one
-  // per thread), so every load of the pass is independent of the others.
-  const double* src = p.gram + (int64_t)(bh * slots + slot) * p.nch * (NT * 256);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = tid % D, part = tid / D, c0 = part * CW;
+  // the node's entry: formed from its rows (root, left child), or the
+  // parent's entry minus the left sibling's (right child)
+  const int pslots = gram_parent_slots(p.level);
+  const int ps = (p.level == 0) ? 0 : (slot >> 1);
+  const double* a_src = p.gram + (int64_t)(bh * pslots + ps) * p.nch * E;
+  const double* par_src =
+      (p.level > 0 && (slot & 1)) ? p.gnode_prev + (int64_t)(bh * pslots + ps) * E : nullptr;
+  // kept for the next depth if this node splits into children that need it
+  double* keep = (p.gram_store && m >= 3) ? p.gnode_cur + (int64_t)(bh * slots + slot) * E : nullptr;
+  const double n = (double)(m * C);
   double* mu = p.mu + ((size_t)bh * G + s) * D;
   double* vv = p.vec + ((size_t)bh * G + s) * D;
-  const double n = (double)(m * C);
   if (tid < D) {
-    mus[tid] = mu[tid];
+    double sx = a_src[NT * 256 + tid];
+    if (par_src != nullptr) sx = par_src[NT * 256 + tid] - sx;
+    if (keep != nullptr) keep[NT * 256 + tid] = sx;
+    const double mv = sx / n;
+    mus[tid] = mv;
+    mu[tid] = mv;
     vec[tid] = 1.0 / sqrt((double)D);
   }
-  __syncthreads();
-  const int li = tid >> 4, lj = tid & 15;
-  int ti = 0, tj = 0;  // tile k = (ti, tj), upper tiles in row-major order
+  double sg[CW];
 #pragma unroll
-  for (int k = 0; k < NT; ++k) {
-    const double a = src[k * 256 + tid];
-    const int i = 16 * ti + li, jj = 16 * tj + lj;
-    const double c = a - n * mus[i] * mus[jj];
-    sig[i * D + jj] = c;
-    sig[jj * D + i] = c;
-    if (++tj == DT) tj = ++ti;
+  for (int c = 0; c < CW; ++c) {
+    const int j = c0 + c;
+    const int I = i >> 4, J = j >> 4;
+    const int off = (I <= J) ? gram_tile_index<DT>(I, J) * 256 + (i & 15) * 16 + (j & 15)
+                             : gram_tile_index<DT>(J, I) * 256 + (j & 15) * 16 + (i & 15);
+    sg[c] = a_src[off];
+  }
+  if (par_src != nullptr) {
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      const int j = c0 + c;
+      const int I = i >> 4, J = j >> 4;
+      const int off = (I <= J) ? gram_tile_index<DT>(I, J) * 256 + (i & 15) * 16 + (j & 15)
+                               : gram_tile_index<DT>(J, I) * 256 + (j & 15) * 16 + (i & 15);
+      sg[c] = par_src[off] - sg[c];
+    }
+  }
+  if (keep != nullptr) {
+    // every upper-tile entry once: (i, j) with tile row <= tile column
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      const int j = c0 + c;
+      const int I = i >> 4, J = j >> 4;
+      if (I <= J) keep[gram_tile_index<DT>(I, J) * 256 + (i & 15) * 16 + (j & 15)] = sg[c];
+    }
   }
   __syncthreads();
-  for (int it = 0; it < p.power_iters; ++it) {
-    // w_i = sum_j Sigma_ij v_j, read down column i (Sigma is stored symmetric,
-    // so the values and their order are those of row i, and consecutive
-    // lanes read consecutive words)
-    double w = 0.0;
-    if (tid < D) {
-      for (int jj = 0; jj < D; ++jj) w = __builtin_fma(sig[jj * D + tid], vec[jj], w);
-    }
-    // |w|^2 summed as a pairwise tree: element i meets i + D/2, then i + D/4,
-    // ..., i + 1 (the first halving across the two waves through LDS, the
-    // rest inside wave 0 by lane shifts)
-    double q = (tid < D) ? w * w : 0.0;
-    if constexpr (D == 128) {
-      if (tid >= 64 && tid < 128) half[lane] = q;
-      __syncthreads();
-      if (tid < 64) q += half[lane];
-    }
-    if (tid < 64) {
+  {
+    const double ni = n * mus[i];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) q += __shfl_down(q, o, 64);
-      if (tid == 0) red[0] = q;
+    for (int c = 0; c < CW; ++c) sg[c] = sg[c] - ni * mus[c0 + c];
+  }
+  for (int it = 0; it < p.power_iters; ++it) {
+    double a[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int c = 0; c < CW; c += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] = __builtin_fma(sg[c + u], vec[c0 + c + u], a[u]);
+    }
+    const double pw = (a[0] + a[1]) + (a[2] + a[3]);
+    if (part > 0) red[part][i] = pw;
+    __syncthreads();
+    double wv = pw;
+    if (part == 0) {
+#pragma unroll
+      for (int q = 1; q < PARTS; ++q) wv += red[q][i];
+      double q2 = wv * wv;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) q2 += __shfl_down(q2, o, 64);
+      if (lane == 0) nrm[w] = q2;
     }
     __syncthreads();
-    const double nrm2 = red[0];
-    if (tid < D && nrm2 > 0.0) vec[tid] = w / sqrt(nrm2);
+    double nrm2 = nrm[0];
+#pragma unroll
+    for (int q = 1; q < NWD; ++q) nrm2 += nrm[q];
+    if (part == 0 && nrm2 > 0.0) vec[i] = wv / sqrt(nrm2);
     __syncthreads();
   }
   // sign rule: the component of largest magnitude (first on ties) positive
@@ -828,18 +923,18 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   __syncthreads();
   for (int o = D / 2; o > 0; o >>= 1) {
     if (tid < o) {
-      const double a = vmag[tid], b = vmag[tid + o];
-      const int ia = vidx[tid], ib = vidx[tid + o];
-      if (b > a || (b == a && ib < ia)) {
-        vmag[tid] = b;
-        vidx[tid] = ib;
+      const double x = vmag[tid], y = vmag[tid + o];
+      const int ix = vidx[tid], iy = vidx[tid + o];
+      if (y > x || (y == x && iy < ix)) {
+        vmag[tid] = y;
+        vidx[tid] = iy;
       }
     }
     __syncthreads();
   }
-  if (tid == vidx[0]) red[0] = nv;
+  if (tid == vidx[0]) nrm[0] = nv;
   __syncthreads();
-  if (red[0] < 0.0) nv = -nv;
+  if (nrm[0] < 0.0) nv = -nv;
   if (tid < D) vv[tid] = nv;
 }
 
@@ -923,23 +1018,23 @@ hipError_t launch_pddp_reduce(int d, int c, int stage, const PddpParams& p, hipS
 }
 
 hipError_t launch_pddp_gram(int d, int c, const PddpParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.bh * ((int64_t)1 << p.level) * p.nch));
+  const int pslots = p.level == 0 ? 1 : 1 << (p.level - 1);
+  const dim3 grid((unsigned)(p.bh * pslots * p.nch));
   if (d == 128 && c == 128) hipLaunchKernelGGL((pddp_gram_kernel<128, 128>), grid, dim3(256), 0, s, p);
   else if (d == 128 && c == 64) hipLaunchKernelGGL((pddp_gram_kernel<128, 64>), grid, dim3(256), 0, s, p);
   else if (d == 64 && c == 128) hipLaunchKernelGGL((pddp_gram_kernel<64, 128>), grid, dim3(256), 0, s, p);
   else if (d == 64 && c == 64) hipLaunchKernelGGL((pddp_gram_kernel<64, 64>), grid, dim3(256), 0, s, p);
   else return hipErrorInvalidValue;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nch < 2) return e;
+  const int nt = (d / 16) * (d / 16 + 1) / 2;
+  const dim3 sgrid((unsigned)(p.bh * pslots * (nt + 1)));
+  if (d == 128) hipLaunchKernelGGL((pddp_gram_sum_kernel<128>), sgrid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((pddp_gram_sum_kernel<64>), sgrid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_pddp_gram_power(int d, int c, const PddpParams& p, hipStream_t s) {
-  const int nt = (d / 16) * (d / 16 + 1) / 2;
-  const dim3 sgrid((unsigned)(p.bh * ((int64_t)1 << p.level) * nt));
-  if (d == 128) hipLaunchKernelGGL((pddp_gram_sum_kernel<128>), sgrid, dim3(256), 0, s, p);
-  else if (d == 64) hipLaunchKernelGGL((pddp_gram_sum_kernel<64>), sgrid, dim3(256), 0, s, p);
-  else return hipErrorInvalidValue;
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(p.bh * ((int64_t)1 << p.level)));
   if (d == 128 && c == 128) hipLaunchKernelGGL((pddp_gram_power_kernel<128, 128>), grid, dim3(256), 0, s, p);
   else if (d == 128 && c == 64) hipLaunchKernelGGL((pddp_gram_power_kernel<128, 64>), grid, dim3(256), 0, s, p);

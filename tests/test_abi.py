@@ -38,11 +38,13 @@ def test_workspace_sizes():
     dm = d()
     G, bh, D = 8, 2, 128
     want = 0
-    # partials, mu, v, projections, second perm, then the covariance-path
-    # chunk partials of its largest depth (depths with nodes of >= 4 groups
-    # for d = 128: depth 1 has 2 node slots of 1 chunk each, 36 upper 16x16
-    # fp64 tiles per chunk)
-    for nbytes in (bh * G * D * 8,) * 3 + (bh * 1024 * 8, bh * 1024 * 4, bh * 2 * 36 * 256 * 8):
+    # partials, mu, v, projections, second perm, then the covariance path:
+    # chunk partials of the formed nodes at the depth that needs most (G = 8,
+    # 3 depths: the root in 1 chunk, 1 left child of 4 groups, 2 left
+    # children of 2 groups: 2 entries) and two buffers of kept entries
+    # (2^(3-2) = 2 slots); an entry is 36 upper 16x16 fp64 tiles + 128 row sums
+    e = (36 * 256 + 128) * 8
+    for nbytes in (bh * G * D * 8,) * 3 + (bh * 1024 * 8, bh * 1024 * 4, bh * 2 * e, bh * 2 * e, bh * 2 * e):
         want = (want + nbytes + 255) // 256 * 256
     assert lib.mcs_group_workspace_bytes(ctypes.byref(dm)) == want
     per_head = (G * 1000 * 4 + 255) // 256 * 256 + (G * 1024 * 4 + 255) // 256 * 256
