@@ -35,7 +35,8 @@
  * Rows n_valid .. n_pad-1 are padding: the caller zero-fills them in Q, K, V;
  * padded keys never take part in a softmax and are never selected; padded
  * query rows take part in grouping as all-zero rows and get O = R = 0, lse = 0.
- * Supported: head_dim in {64, 128}; group_size C in {64, 128}; n_pad a
+ * Supported: head_dim in {64, 96, 128} (the k-means comparator and the block
+ * selection variants: 64 and 128); group_size C in {64, 128}; n_pad a
  * multiple of C; 1 <= n_valid <= n_pad < 2^24; 1 <= topk <= n_valid;
  * batch*heads*n_pad*head_dim < 2^40.  Every pointer must be 16-byte aligned.
  *
@@ -116,9 +117,10 @@ const char* mcs_last_error(void);
  * index on ties) and its members ordered by (projection, token index); the
  * first floor(m/2)*C go to the left child, the rest to the right.  All nodes of
  * one depth, across all heads, are processed by the same launches and only the
- * index array moves between depths.  Arithmetic is fp64 on the bf16 inputs; at
- * depths with large nodes the iteration runs on the node's centred covariance
- * (X^T X - n mu mu^T, formed once), the same operator as on the rows.
+ * index array moves between depths.  Arithmetic is fp64 on the bf16 inputs; the
+ * iteration runs on each node's centred covariance (X^T X - n mu mu^T), the
+ * same operator as on the rows, with X^T X formed for one child of every split
+ * and taken for the other as the parent's minus it.
  *   q          : bf16 [B,H,n_pad,d], the anchor step's queries (padding rows 0)
  *   power_iters: 0 .. 1000 (20 in the method's configurations)
  *   max_levels : -1 = all ceil(log2(n_pad/C)) depths; 0..L = stop after that

@@ -97,18 +97,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   // plane ins/4, tile slots 16*(ins%4) .. +15; lane l writes slot
   // 16*(ins%4) + l/4, physical chunk l%4, i.e. logical chunk (l%4)^((l/16)%4)
   // of that plane.  Slot 16*r + j holds key 4*j + r of the tile, so a lane's
-  // copies need the consecutive keys 4*(l/4) + r0 + i (r0 = (w*IPW)%4): one
-  // offset register serves all its index loads.  Any fixed order of the keys
-  // inside a tile is valid, as K and V share it and only the final-tile mask
-  // looks at key positions.  K, V and the index row are read through buffer
-  // resources with 32-bit offsets (row * row stride, a 24-bit multiply);
-  // reads past a resource's end return zero, which the final-tile mask covers
-  // for the index row.
+  // i-th copy needs key 4*(l/4) + (ins%4): one offset register serves all its
+  // index loads, the wave-uniform key and plane parts coming from ins.  Any
+  // fixed order of the keys inside a tile is valid, as K and V share it and
+  // only the final-tile mask looks at key positions.  K, V and the index row
+  // are read through buffer resources with 32-bit offsets (row * row stride,
+  // a 24-bit multiply); reads past a resource's end return zero, which the
+  // final-tile mask covers for the index row.
   constexpr int NTOK = IPW < 4 ? IPW : 4;     // distinct keys per lane per tile
-  const int r0 = (w * IPW) & 3;
+  auto ins_key = [&](int i) { return (w * IPW + i) & 3; };                  // key offset of copy i
+  auto ins_plane = [&](int i) { return (uint32_t)((w * IPW + i) >> 2) * 64u; };  // its plane's byte offset
   const int j4 = 4 * (lane >> 2);
   const uint32_t gcb = 16u * (uint32_t)((lane ^ (lane >> 4)) & 3);
-  const uint32_t plane_soff = (uint32_t)((w * IPW) >> 2) * 64u;
   const uint32_t rsb = (uint32_t)p.sk.n * 2u;  // row stride of K and V in bytes
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, head_span_bytes(p.sk, p.n_pad, D));
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, head_span_bytes(p.sv, p.n_pad, D));
@@ -116,13 +116,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
       (MODE == ATTN_DENSE) ? krs : make_rsrc(idxrow, (uint32_t)nk * 4u);
   int tok[NTOK];
   auto fetch_idx = [&](int t) {
-    const int key0 = t * KT + j4 + r0;
+    const int key0 = t * KT + j4;
 #pragma unroll
     for (int i = 0; i < NTOK; ++i) {
       if (MODE == ATTN_DENSE) {
-        tok[i] = key0 + i;
+        tok[i] = key0 + ins_key(i);
       } else {
-        tok[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, (uint32_t)(key0 + i) * 4u, 0, 0);
+        tok[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, (uint32_t)(key0 + ins_key(i)) * 4u, 0, 0);
       }
     }
   };
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const uint32_t voff = __umul24((uint32_t)tok[i % NTOK], rsb) + gcb;
-      gather16_buf(krs, kdst + i * 1024, voff, plane_soff + (i >> 2) * 64);
-      gather16_buf(vrs, vdst + i * 1024, voff, plane_soff + (i >> 2) * 64);
+      gather16_buf(krs, kdst + i * 1024, voff, ins_plane(i));
+      gather16_buf(vrs, vdst + i * 1024, voff, ins_plane(i));
     }
   };
 
@@ -202,9 +202,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
           const int i = c >> 1;
           const uint32_t voff = __umul24((uint32_t)tok[i % NTOK], rsb) + gcb;
           if (c & 1)
-            gather16_buf(vrs, kdst_n + TILE + i * 1024, voff, plane_soff + (i >> 2) * 64);
+            gather16_buf(vrs, kdst_n + TILE + i * 1024, voff, ins_plane(i));
           else
-            gather16_buf(krs, kdst_n + i * 1024, voff, plane_soff + (i >> 2) * 64);
+            gather16_buf(krs, kdst_n + i * 1024, voff, ins_plane(i));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -396,6 +396,8 @@ template <int MODE>
 static hipError_t launch_mode(int d, int c, const AttnParams& p, hipStream_t s) {
   if (d == 128 && c == 128) return launch_one<128, 128, MODE>(p, s);
   if (d == 128 && c == 64) return launch_one<128, 64, MODE>(p, s);
+  if (d == 96 && c == 128) return launch_one<96, 128, MODE>(p, s);
+  if (d == 96 && c == 64) return launch_one<96, 64, MODE>(p, s);
   if (d == 64 && c == 128) return launch_one<64, 128, MODE>(p, s);
   if (d == 64 && c == 64) return launch_one<64, 64, MODE>(p, s);
   return hipErrorInvalidValue;

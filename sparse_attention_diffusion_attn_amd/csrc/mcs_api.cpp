@@ -55,8 +55,8 @@ int32_t check_dims(const mcs_dims* d) {
   if (d == nullptr) return fail(MCS_ERR_INVALID_ARG, "dims is NULL");
   if (d->batch < 1 || d->heads < 1)
     return fail(MCS_ERR_INVALID_ARG, "batch (%d) and heads (%d) must be >= 1", d->batch, d->heads);
-  if (d->head_dim != 64 && d->head_dim != 128)
-    return fail(MCS_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128)
+    return fail(MCS_ERR_UNSUPPORTED, "head_dim %d not supported (64, 96 or 128)", d->head_dim);
   if (d->group_size != 64 && d->group_size != 128)
     return fail(MCS_ERR_UNSUPPORTED, "group_size %d not supported (64 or 128)", d->group_size);
   if (d->n_pad < 1 || d->n_pad >= (1 << 24))
@@ -248,6 +248,8 @@ GroupWs group_ws(const mcs_dims* d) {
 
 // ---- size-balanced k-means grouping ----
 int32_t check_kmeans(const mcs_dims* d) {
+  if (d->head_dim == 96)
+    return fail(MCS_ERR_UNSUPPORTED, "k-means grouping supports head_dim 64 and 128");
   const int G = d->n_pad / d->group_size;
   if (G > mcs::KM_MAX_GROUPS)
     return fail(MCS_ERR_UNSUPPORTED, "k-means grouping supports up to %d groups per head (got %d)",
@@ -285,6 +287,8 @@ size_t scores_per_head(const mcs_dims* d) {
 
 // ---- block selection ----
 int32_t check_blocks(const mcs_dims* d, int32_t mode, int32_t block, int32_t nblocks) {
+  if (d->head_dim == 96)
+    return fail(MCS_ERR_UNSUPPORTED, "block selection supports head_dim 64 and 128");
   if (mode != MCS_BLOCK_EXACT && mode != MCS_BLOCK_MEANPOOL)
     return fail(MCS_ERR_INVALID_ARG, "block selection mode %d unknown", mode);
   if (block < 1 || block > d->n_valid)
@@ -440,7 +444,7 @@ int32_t mcs_group_strided(const mcs_dims* dims, const mcs_layout* layout, const 
     } else {
       // no iterations: v stays v0; only the node means are needed
       MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 0, p, s), "pddp mean"));
-      MCS_TRY(hip_status(mcs::launch_pddp_reduce(d, c, 0, p, s), "pddp mean reduce"));
+      MCS_TRY(hip_status(mcs::launch_pddp_mean(d, c, p, s), "pddp mean reduce"));
     }
     MCS_TRY(hip_status(mcs::launch_pddp_partial(d, c, 2, p, s), "pddp projection"));
     MCS_TRY(hip_status(mcs::launch_pddp_split(c, p, s), "pddp split"));

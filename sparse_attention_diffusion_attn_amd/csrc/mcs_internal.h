@@ -103,7 +103,6 @@ struct PddpParams {
   int64_t bh;
   int32_t heads;
   int32_t n_pad, groups, level;
-  int32_t fix_sign;       // reduce stage 1: apply the sign rule to v (last power step)
   // covariance path; an entry is the upper 16x16 tiles of X^T X then the d
   // row sums (gram_entry doubles)
   double* gram;           // chunk partials of the formed nodes [BH, parent slots, nch, entry]
@@ -146,13 +145,12 @@ hipError_t launch_meanpool_scores(int head_dim, int group_size, const BlockParam
 hipError_t launch_expand_blocks(const BlockParams& p, hipStream_t s);
 
 hipError_t launch_pddp_identity(const PddpParams& p, hipStream_t s);
-// stage: 0 = node means, 1 = one power-iteration step, 2 = projections
+// stage: 0 = per-block row sums (node means without power iterations),
+// 2 = projections
 hipError_t launch_pddp_partial(int head_dim, int group_size, int stage, const PddpParams& p,
                                hipStream_t s);
-// stage: 0 = finish means and set v0, 1 = finish a power-iteration step
-// (and, with p.fix_sign, make v's largest-magnitude component positive)
-hipError_t launch_pddp_reduce(int head_dim, int group_size, int stage, const PddpParams& p,
-                              hipStream_t s);
+// node means from the stage-0 sums, v = v0 (no power iterations)
+hipError_t launch_pddp_mean(int head_dim, int group_size, const PddpParams& p, hipStream_t s);
 hipError_t launch_pddp_split(int group_size, const PddpParams& p, hipStream_t s);
 // Covariance path of a depth: X^T X and the row sums of the formed nodes (the
 // root, else the left children), chunk partials summed per node

@@ -110,34 +110,40 @@ __device__ __forceinline__ double add_xor32(double x) {
   return a + b;
 }
 
-// stage 0: partial[g] = sum of the block's rows
-// stage 1: partial[g] = sum_r ((x_r - mu) . v) (x_r - mu)
+// stage 0: partial[g] = sum of the block's rows (node means when no power
+//          iterations run)
 // stage 2: proj[pos] = (x_r - mu) . v (v with its sign already fixed)
 //
 // Persistent: workgroup i handles the C-row blocks i, i + P, i + 2P, ... (P =
 // grid size, all resident), each block being one group of perm (block b =
-// head b / G, group b % G).  Thread (dg, rg) owns dimensions 8dg .. 8dg+7 of
-// the rows rg, rg + RG, ... of a block and keeps them in VGPRs (bf16); the DG
-// threads of a row are consecutive lanes.  While block b is computed, the rows
-// of block b + P (and the perm indices of block b + 2P) are loading, and the
-// node's mu / v of block b + P are copied into the other half of a
+// head b / G, group b % G).  Thread (dg, rg) owns dimensions DPL*dg ..
+// DPL*dg + DPL-1 of the rows rg, rg + RG, ... of a block and keeps them in
+// VGPRs (bf16; DPL = 8, or 12 for d = 96 with 8 lanes per row); the DG
+// threads of a row are consecutive lanes.  While block b is computed, the
+// rows of block b + P (and the perm indices of block b + 2P) are loading, and
+// the node's mu / v of block b + P are copied into the other half of a
 // double-buffered LDS pair, so the workgroup never waits on a dependent load
 // chain.  Reductions: per-row dot products over the DG lanes of the row with
 // DPP moves; per-dimension sums over a wavefront's row groups with lane swaps,
 // then over the four wavefronts in LDS (fixed orders throughout).
 //
-// Arithmetic (fp64): with c = mu . v,
-//   t_r = (x_r - mu) . v = x_r . v - c
-//   sum_r t_r (x_r - mu) = sum_r t_r x_r - mu sum_r t_r
-// (the same sums, regrouped so that every element costs one FMA per pass).
+// With c = mu . v, t_r = (x_r - mu) . v = x_r . v - c.
+template <int D>
+struct RowLayout {
+  static constexpr int DPL = (D == 96) ? 12 : 8;  // dimensions per lane
+  static constexpr int DG = D / DPL;              // lanes per row
+  static constexpr int W4 = DPL / 2;              // 32-bit words per lane
+};
+
 template <int D, int C, int STAGE>
 __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   constexpr int NT = 256;
-  constexpr int DG = D / 8, RG = NT / DG, RPT = C / RG;
+  constexpr int DPL = RowLayout<D>::DPL, DG = RowLayout<D>::DG, W4 = RowLayout<D>::W4;
+  constexpr int RG = NT / DG, RPT = C / RG;
   static_assert(DG == 8 || DG == 16, "row lanes");
+  static_assert(STAGE == 0 || STAGE == 2, "stage");
   __shared__ __attribute__((aligned(16))) double muv[2][2][128];  // [buf][mu | v][d]
   __shared__ double part[NT / 64][D];
-
   const int G = p.groups;
   const int64_t nblk = p.bh * (int64_t)G;
   const int tid = threadIdx.x;
@@ -176,33 +182,44 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
 #pragma unroll
     for (int k = 0; k < RPT; ++k) ix[k] = pc[rg + k * RG];
   };
-  // this thread's 8 bf16 of each of its rows (16 bytes each)
-  auto load_rows = [&](Pos q, const int (&ix)[RPT], uint4 (&xr)[RPT]) {
+  // this thread's DPL bf16 of each of its rows (16 bytes, or 16 + 8)
+  struct Row {
+    uint32_t u[W4];
+  };
+  auto load_rows = [&](Pos q, const int (&ix)[RPT], Row (&xr)[RPT]) {
     const uint16_t* Qb = p.q + head_offset(p.sq, q.bh, p.heads);
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) xr[k] = *(const uint4*)(Qb + (int64_t)ix[k] * p.sq.n + 8 * dg);
+    for (int k = 0; k < RPT; ++k) {
+      const uint16_t* src = Qb + (int64_t)ix[k] * p.sq.n + DPL * dg;
+      const uint4 a = *(const uint4*)src;
+      xr[k].u[0] = a.x; xr[k].u[1] = a.y; xr[k].u[2] = a.z; xr[k].u[3] = a.w;
+      if constexpr (W4 == 6) {
+        const uint2 b = *(const uint2*)(src + 8);
+        xr[k].u[4] = b.x; xr[k].u[5] = b.y;
+      }
+    }
   };
   // mu and v of the node starting at group s into LDS half `buf` (one 16-byte
-  // copy per lane of waves 0 and 1; for D = 64 the upper half is not used)
+  // copy per lane of waves 0 and 1; for D < 128 the upper part is not used)
   auto load_muv = [&](Pos q, int s, int buf) {
     if (STAGE == 0 || w > 1) return;
     const uint32_t off = (uint32_t)((((int64_t)q.bh * G + s) * D) * 8) + 16u * (uint32_t)lane;
     if (w == 0) gather16_buf(murs, &muv[buf][0][0], off, 0);
     else gather16_buf(vrs, &muv[buf][1][0], off, 0);
   };
-  auto to_f64 = [&](const uint4& xv, double (&x)[8]) {
-    const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+  auto to_f64 = [&](const Row& xv, double (&x)[DPL]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = (double)__uint_as_float(w4[e] << 16);
-      x[2 * e + 1] = (double)__uint_as_float(w4[e] & 0xffff0000u);
+    for (int e = 0; e < W4; ++e) {
+      x[2 * e] = (double)__uint_as_float(xv.u[e] << 16);
+      x[2 * e + 1] = (double)__uint_as_float(xv.u[e] & 0xffff0000u);
     }
   };
-  // per-dimension block totals: acc[e] (dimension 8dg+e, this thread's rows)
-  // summed over the wavefront's row groups, then over the wavefronts in order
-  auto store_totals = [&](int bh, int g, double (&acc)[8]) {
+  // per-dimension block totals: acc[e] (dimension DPL*dg+e, this thread's
+  // rows) summed over the wavefront's row groups, then over the wavefronts in
+  // order
+  auto store_totals = [&](int bh, int g, double (&acc)[DPL]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < DPL; ++e) {
       double x = acc[e];
       if (DG == 8) x += dpp_f64<0x128>(x);  // row_ror:8 = lane ^ 8 inside a 16-lane row
       x = add_xor16(x);
@@ -211,7 +228,7 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
     }
     if (lane < DG) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[w][8 * dg + e] = acc[e];
+      for (int e = 0; e < DPL; ++e) part[w][DPL * dg + e] = acc[e];
     }
     __syncthreads();
     if (tid < D) {
@@ -229,7 +246,7 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   int s, m, s_n = 0, m_n = 0;
   node_of(G, p.level, cur.g, s, m);
   int idx_n[RPT];
-  uint4 xr[RPT], xr_n[RPT];
+  Row xr[RPT], xr_n[RPT];
   load_idx(cur, idx_n);
   wait_vm0();
   load_rows(cur, idx_n, xr);
@@ -250,59 +267,37 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
     const int bh = cur.bh;
     const int g = cur.g;
     if (m >= 2) {
-      double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (STAGE == 0) {
+        double acc[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = 0.0;
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
-          double x[8];
+          double x[DPL];
           to_f64(xr[k], x);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += x[e];
+          for (int e = 0; e < DPL; ++e) acc[e] += x[e];
         }
         store_totals(bh, g, acc);
       } else {
-        double mu8[8], v8[8];
+        double mu8[DPL], v8[DPL];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          mu8[e] = muv[buf][0][8 * dg + e];
-          v8[e] = muv[buf][1][8 * dg + e];
+        for (int e = 0; e < DPL; ++e) {
+          mu8[e] = muv[buf][0][DPL * dg + e];
+          v8[e] = muv[buf][1][DPL * dg + e];
         }
         double c = 0.0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) c = __builtin_fma(mu8[e], v8[e], c);
-        if (STAGE == 1) {
-          // one conversion per row: t_r = x_r . v - c over the DG lanes of the
-          // row, then acc += t_r x_r from the same registers (the sums run
-          // over the rows in the same order as a separate second sweep would)
-          double tsum = 0.0;
-#pragma unroll
-          for (int k = 0; k < RPT; ++k) {
-            double x[8];
-            to_f64(xr[k], x);
-            double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              a0 = __builtin_fma(x[e], v8[e], a0);
-              a1 = __builtin_fma(x[e + 1], v8[e + 1], a1);
-            }
-            const double tk = group_sum<DG>((a0 + a1) - c);
-            tsum += tk;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(tk, x[e], acc[e]);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fma(-mu8[e], tsum, acc[e]);
-          store_totals(bh, g, acc);
-        } else {
+        for (int e = 0; e < DPL; ++e) c = __builtin_fma(mu8[e], v8[e], c);
         // t_r = x_r . v - c summed over the DG lanes of row r
         double t[RPT];
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
-          double x[8];
+          double x[DPL];
           to_f64(xr[k], x);
           double a0 = 0.0, a1 = 0.0;
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
+          for (int e = 0; e < DPL; e += 2) {
             a0 = __builtin_fma(x[e], v8[e], a0);
             a1 = __builtin_fma(x[e + 1], v8[e + 1], a1);
           }
@@ -312,7 +307,6 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
           double* pr = p.proj + (size_t)bh * p.n_pad + (size_t)g * C;
 #pragma unroll
           for (int k = 0; k < RPT; ++k) pr[rg + k * RG] = t[k];
-        }
         }
       }
     }
@@ -326,21 +320,16 @@ __global__ __launch_bounds__(256) void pddp_partial_kernel(PddpParams p) {
   }
 }
 
-// stage 0: mu = (sum of partials) / rows, v = v0 = 1/sqrt(D)
-// stage 1: w = sum of partials; v = w / |w| if |w| > 0; after the last power
-//          step (p.fix_sign) the component of largest magnitude (first on
-//          ties) is made positive.
-// One workgroup of D*PARTS threads per node (PARTS chosen per depth from the
-// largest node size): thread (d, part) sums the partials of groups s + part,
-// s + part + PARTS, ... in that order (independent loads, one dependent add
-// chain), then the PARTS sums of each d in order.
-template <int D, int C, int STAGE, int PARTS>
+// Node means when no power iterations run: mu = (sum of partials) / rows and
+// v = v0 = 1/sqrt(D).  One workgroup of D*PARTS threads per node (PARTS
+// chosen per depth from the largest node size): thread (d, part) sums the
+// partials of groups s + part, s + part + PARTS, ... in that order
+// (independent loads, one dependent add chain), then the PARTS sums of each d
+// in order.
+template <int D, int C, int PARTS>
 __global__ __launch_bounds__(D * PARTS) void pddp_reduce_kernel(PddpParams p) {
   constexpr int NT = D * PARTS;
   __shared__ double part_sum[NT];
-  __shared__ double sq[NT];
-  __shared__ double vmag[D];
-  __shared__ int vidx[D];
   const int G = p.groups;
   const int slots = 1 << p.level;
   const int64_t bh = blockIdx.x / slots;
@@ -361,51 +350,12 @@ __global__ __launch_bounds__(D * PARTS) void pddp_reduce_kernel(PddpParams p) {
   for (; gg < m; gg += PARTS) acc += src[(size_t)gg * D];
   part_sum[tid] = acc;
   __syncthreads();
-  double tot = 0.0;
   if (tid < D) {
-    tot = part_sum[tid];
+    double tot = part_sum[tid];
     for (int q = 1; q < PARTS; ++q) tot += part_sum[q * D + tid];
+    p.mu[((size_t)bh * G + s) * D + tid] = tot / (double)(m * C);
+    p.vec[((size_t)bh * G + s) * D + tid] = 1.0 / sqrt((double)D);
   }
-  double* mu = p.mu + ((size_t)bh * G + s) * D;
-  double* vv = p.vec + ((size_t)bh * G + s) * D;
-  if (STAGE == 0) {
-    if (tid < D) {
-      mu[tid] = tot / (double)(m * C);
-      vv[tid] = 1.0 / sqrt((double)D);
-    }
-    return;
-  }
-  sq[tid] = (tid < D) ? tot * tot : 0.0;
-  __syncthreads();
-  for (int o = NT / 2; o > 0; o >>= 1) {
-    if (tid < o) sq[tid] += sq[tid + o];
-    __syncthreads();
-  }
-  const double nrm2 = sq[0];
-  double nv = 0.0;
-  if (tid < D) nv = (nrm2 > 0.0) ? tot / sqrt(nrm2) : vv[tid];
-  if (p.fix_sign) {
-    if (tid < D) {
-      vmag[tid] = fabs(nv);
-      vidx[tid] = tid;
-    }
-    __syncthreads();
-    for (int o = D / 2; o > 0; o >>= 1) {
-      if (tid < o) {
-        const double a = vmag[tid], b = vmag[tid + o];
-        const int ia = vidx[tid], ib = vidx[tid + o];
-        if (b > a || (b == a && ib < ia)) {
-          vmag[tid] = b;
-          vidx[tid] = ib;
-        }
-      }
-      __syncthreads();
-    }
-    if (tid == vidx[0]) sq[0] = nv;   // the signed value of the largest component
-    __syncthreads();
-    if (sq[0] < 0.0) nv = -nv;
-  }
-  if (tid < D) vv[tid] = nv;
 }
 
 template <int NT>
@@ -807,24 +757,28 @@ __global__ __launch_bounds__(256) void pddp_gram_sum_kernel(PddpParams p) {
   src[0] = a;
 }
 
-// One workgroup of 256 threads per node.  Thread (i, part), i = t % D, part =
-// t / D, holds row i, columns part*D/PARTS .. +D/PARTS-1 of the centred
-// matrix in registers (64 values for d = 128, 16 for d = 64), so the kernel
-// needs almost no LDS and several nodes share a CU.  One step: each thread's
-// partial dot product with v (four interleaved accumulators, v read from LDS
-// as a broadcast), the PARTS partials of row i summed in part order, |w|^2
-// summed over the wavefronts of part 0, v = w / |w|.
+// One workgroup of 256 threads per node.  The node's entry is staged through
+// LDS (coalesced loads, one tile of 256 values per pass; inside a tile, entry
+// (r, c) sits at r*16 + (c ^ r), so both the row reads and the mirrored column
+// reads below are free of bank conflicts).  Thread (i, part), i = t % D, part
+// = t / D, then holds row i, columns part*D/PARTS .. +D/PARTS-1 of the centred
+// matrix in registers (64 values for d = 128, 16 for d = 64); upper tiles are
+// read along their rows, lower ones as the mirrored upper tile's columns.
+// One step: each thread's partial dot product with v (four interleaved
+// accumulators, v read from LDS as a broadcast), the PARTS partials of row i
+// summed in part order, |w|^2 summed over the wavefronts of part 0 (lane
+// moves in the VALU, then the wavefronts in order), v = w / |w|.
 template <int D, int C>
 __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   constexpr int DT = D / 16, NT = DT * (DT + 1) / 2, E = gram_entry<D>();
-  constexpr int PARTS = 256 / D, CW = D / PARTS, NWD = D / 64;
-  static_assert(CW % 4 == 0, "columns per thread");
+  constexpr int PARTS = 256 / D, CW = D / PARTS, NWD = (D + 63) / 64;
+  constexpr int P2 = D <= 64 ? 64 : 128;  // sign rule: tree over the next power of two
+  static_assert(CW % 16 == 0 && CW * PARTS == D, "columns per thread");
+  __shared__ double stage[NT * 256];   // the entry's tiles; later the sign rule's scratch
   __shared__ double vec[D];
   __shared__ double mus[D];
-  __shared__ double red[PARTS][D];
+  __shared__ double red[PARTS - 1][D];
   __shared__ double nrm[NWD];
-  __shared__ double vmag[D];
-  __shared__ int vidx[D];
   const int G = p.groups;
   const int slots = 1 << p.level;
   const int bh = blockIdx.x / slots;
@@ -832,7 +786,10 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   int s, m;
   if (!node_of_slot(G, p.level, slot, s, m) || m < 2) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int i = tid % D, part = tid / D, c0 = part * CW;
+  // threads past PARTS*D (d = 96: the last 64) hold no matrix entries
+  const int i = tid % D, part = tid / D;
+  const bool active = part < PARTS;
+  const int c0 = active ? part * CW : 0;
   // the node's entry: formed from its rows (root, left child), or the
   // parent's entry minus the left sibling's (right child)
   const int pslots = gram_parent_slots(p.level);
@@ -845,6 +802,22 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
   const double n = (double)(m * C);
   double* mu = p.mu + ((size_t)bh * G + s) * D;
   double* vv = p.vec + ((size_t)bh * G + s) * D;
+  {
+    double x[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) x[k] = a_src[k * 256 + tid];
+    if (par_src != nullptr) {
+#pragma unroll
+      for (int k = 0; k < NT; ++k) x[k] = par_src[k * 256 + tid] - x[k];
+    }
+    if (keep != nullptr) {
+#pragma unroll
+      for (int k = 0; k < NT; ++k) keep[k * 256 + tid] = x[k];
+    }
+    const int r = tid >> 4, c = tid & 15;
+#pragma unroll
+    for (int k = 0; k < NT; ++k) stage[k * 256 + r * 16 + (c ^ r)] = x[k];
+  }
   if (tid < D) {
     double sx = a_src[NT * 256 + tid];
     if (par_src != nullptr) sx = par_src[NT * 256 + tid] - sx;
@@ -854,36 +827,25 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
     mu[tid] = mv;
     vec[tid] = 1.0 / sqrt((double)D);
   }
-  double sg[CW];
-#pragma unroll
-  for (int c = 0; c < CW; ++c) {
-    const int j = c0 + c;
-    const int I = i >> 4, J = j >> 4;
-    const int off = (I <= J) ? gram_tile_index<DT>(I, J) * 256 + (i & 15) * 16 + (j & 15)
-                             : gram_tile_index<DT>(J, I) * 256 + (j & 15) * 16 + (i & 15);
-    sg[c] = a_src[off];
-  }
-  if (par_src != nullptr) {
-#pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      const int j = c0 + c;
-      const int I = i >> 4, J = j >> 4;
-      const int off = (I <= J) ? gram_tile_index<DT>(I, J) * 256 + (i & 15) * 16 + (j & 15)
-                               : gram_tile_index<DT>(J, I) * 256 + (j & 15) * 16 + (i & 15);
-      sg[c] = par_src[off] - sg[c];
-    }
-  }
-  if (keep != nullptr) {
-    // every upper-tile entry once: (i, j) with tile row <= tile column
-#pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      const int j = c0 + c;
-      const int I = i >> 4, J = j >> 4;
-      if (I <= J) keep[gram_tile_index<DT>(I, J) * 256 + (i & 15) * 16 + (j & 15)] = sg[c];
-    }
-  }
   __syncthreads();
+  double sg[CW];
   {
+    const int I = i >> 4, ii = i & 15;
+#pragma unroll
+    for (int jb = 0; jb < CW / 16; ++jb) {
+      const int J = (c0 >> 4) + jb;
+      if (I <= J) {
+        // row ii of upper tile (I, J)
+        const double* t = stage + gram_tile_index<DT>(I, J) * 256 + ii * 16;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) sg[jb * 16 + c] = t[c ^ ii];
+      } else {
+        // column ii of upper tile (J, I)
+        const double* t = stage + gram_tile_index<DT>(J, I) * 256;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) sg[jb * 16 + c] = t[c * 16 + (ii ^ c)];
+      }
+    }
     const double ni = n * mus[i];
 #pragma unroll
     for (int c = 0; c < CW; ++c) sg[c] = sg[c] - ni * mus[c0 + c];
@@ -896,15 +858,17 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
       for (int u = 0; u < 4; ++u) a[u] = __builtin_fma(sg[c + u], vec[c0 + c + u], a[u]);
     }
     const double pw = (a[0] + a[1]) + (a[2] + a[3]);
-    if (part > 0) red[part][i] = pw;
+    if (part > 0 && active) red[part - 1][i] = pw;
     __syncthreads();
     double wv = pw;
     if (part == 0) {
 #pragma unroll
-      for (int q = 1; q < PARTS; ++q) wv += red[q][i];
-      double q2 = wv * wv;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) q2 += __shfl_down(q2, o, 64);
+      for (int q = 1; q < PARTS; ++q) wv += red[q - 1][i];
+    }
+    // |w|^2 over the rows held by part 0 (whole wavefronts take part; the
+    // others add zeros)
+    if (w < NWD) {
+      const double q2 = add_xor32(add_xor16(group_sum<16>(part == 0 ? wv * wv : 0.0)));
       if (lane == 0) nrm[w] = q2;
     }
     __syncthreads();
@@ -915,13 +879,15 @@ __global__ __launch_bounds__(256) void pddp_gram_power_kernel(PddpParams p) {
     __syncthreads();
   }
   // sign rule: the component of largest magnitude (first on ties) positive
+  double* vmag = stage;
+  int* vidx = reinterpret_cast<int*>(stage + P2);
   double nv = (tid < D) ? vec[tid] : 0.0;
-  if (tid < D) {
-    vmag[tid] = fabs(nv);
+  if (tid < P2) {
+    vmag[tid] = (tid < D) ? fabs(nv) : -1.0;  // padding entries never win
     vidx[tid] = tid;
   }
   __syncthreads();
-  for (int o = D / 2; o > 0; o >>= 1) {
+  for (int o = P2 / 2; o > 0; o >>= 1) {
     if (tid < o) {
       const double x = vmag[tid], y = vmag[tid + o];
       const int ix = vidx[tid], iy = vidx[tid + o];
@@ -972,76 +938,82 @@ static hipError_t partial_one(const PddpParams& p, hipStream_t s) {
 template <int D, int C>
 static hipError_t partial_t(int stage, const PddpParams& p, hipStream_t s) {
   if (stage == 0) return partial_one<D, C, 0>(p, s);
-  if (stage == 1) return partial_one<D, C, 1>(p, s);
-  return partial_one<D, C, 2>(p, s);
+  if (stage == 2) return partial_one<D, C, 2>(p, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_pddp_partial(int d, int c, int stage, const PddpParams& p, hipStream_t s) {
   if (d == 128 && c == 128) return partial_t<128, 128>(stage, p, s);
   if (d == 128 && c == 64) return partial_t<128, 64>(stage, p, s);
+  if (d == 96 && c == 128) return partial_t<96, 128>(stage, p, s);
+  if (d == 96 && c == 64) return partial_t<96, 64>(stage, p, s);
   if (d == 64 && c == 128) return partial_t<64, 128>(stage, p, s);
   if (d == 64 && c == 64) return partial_t<64, 64>(stage, p, s);
   return hipErrorInvalidValue;
 }
 
-template <int D, int C, int PARTS>
-static void reduce_one(int stage, const PddpParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.bh << p.level));
-  if (stage == 0) hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 0, PARTS>), grid, dim3(D * PARTS), 0, s, p);
-  else hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 1, PARTS>), grid, dim3(D * PARTS), 0, s, p);
-}
-
 template <int D, int C>
-static hipError_t reduce_t(int stage, const PddpParams& p, hipStream_t s) {
+static hipError_t mean_t(const PddpParams& p, hipStream_t s) {
   // about 8 partials per thread for the largest node of this depth
   const int m_max = (p.groups + (1 << p.level) - 1) >> p.level;
   int parts = 1;
-  while (parts < 1024 / D && parts * 8 < m_max) parts *= 2;
+  while (parts < 1024 / D && parts < 8 && parts * 8 < m_max) parts *= 2;
+  const dim3 grid((unsigned)(p.bh << p.level));
   switch (parts) {
-    case 1: reduce_one<D, C, 1>(stage, p, s); break;
-    case 2: reduce_one<D, C, 2>(stage, p, s); break;
-    case 4: reduce_one<D, C, 4>(stage, p, s); break;
-    case 8: reduce_one<D, C, 8>(stage, p, s); break;
-    default:
-      if constexpr (D * 16 <= 1024) reduce_one<D, C, 16>(stage, p, s);
-      else reduce_one<D, C, 8>(stage, p, s);
+    case 1: hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 1>), grid, dim3(D), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 2>), grid, dim3(D * 2), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 4>), grid, dim3(D * 4), 0, s, p); break;
+    default: hipLaunchKernelGGL((pddp_reduce_kernel<D, C, 8>), grid, dim3(D * 8), 0, s, p); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_pddp_reduce(int d, int c, int stage, const PddpParams& p, hipStream_t s) {
-  if (d == 128 && c == 128) return reduce_t<128, 128>(stage, p, s);
-  if (d == 128 && c == 64) return reduce_t<128, 64>(stage, p, s);
-  if (d == 64 && c == 128) return reduce_t<64, 128>(stage, p, s);
-  if (d == 64 && c == 64) return reduce_t<64, 64>(stage, p, s);
+hipError_t launch_pddp_mean(int d, int c, const PddpParams& p, hipStream_t s) {
+  if (d == 128 && c == 128) return mean_t<128, 128>(p, s);
+  if (d == 128 && c == 64) return mean_t<128, 64>(p, s);
+  if (d == 96 && c == 128) return mean_t<96, 128>(p, s);
+  if (d == 96 && c == 64) return mean_t<96, 64>(p, s);
+  if (d == 64 && c == 128) return mean_t<64, 128>(p, s);
+  if (d == 64 && c == 64) return mean_t<64, 64>(p, s);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_pddp_gram(int d, int c, const PddpParams& p, hipStream_t s) {
+template <int D, int C>
+static hipError_t gram_t(const PddpParams& p, hipStream_t s) {
   const int pslots = p.level == 0 ? 1 : 1 << (p.level - 1);
-  const dim3 grid((unsigned)(p.bh * pslots * p.nch));
-  if (d == 128 && c == 128) hipLaunchKernelGGL((pddp_gram_kernel<128, 128>), grid, dim3(256), 0, s, p);
-  else if (d == 128 && c == 64) hipLaunchKernelGGL((pddp_gram_kernel<128, 64>), grid, dim3(256), 0, s, p);
-  else if (d == 64 && c == 128) hipLaunchKernelGGL((pddp_gram_kernel<64, 128>), grid, dim3(256), 0, s, p);
-  else if (d == 64 && c == 64) hipLaunchKernelGGL((pddp_gram_kernel<64, 64>), grid, dim3(256), 0, s, p);
-  else return hipErrorInvalidValue;
+  hipLaunchKernelGGL((pddp_gram_kernel<D, C>), dim3((unsigned)(p.bh * pslots * p.nch)), dim3(256), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nch < 2) return e;
-  const int nt = (d / 16) * (d / 16 + 1) / 2;
-  const dim3 sgrid((unsigned)(p.bh * pslots * (nt + 1)));
-  if (d == 128) hipLaunchKernelGGL((pddp_gram_sum_kernel<128>), sgrid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((pddp_gram_sum_kernel<64>), sgrid, dim3(256), 0, s, p);
+  constexpr int nt = (D / 16) * (D / 16 + 1) / 2;
+  hipLaunchKernelGGL((pddp_gram_sum_kernel<D>), dim3((unsigned)(p.bh * pslots * (nt + 1))), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pddp_gram(int d, int c, const PddpParams& p, hipStream_t s) {
+  if (d == 128 && c == 128) return gram_t<128, 128>(p, s);
+  if (d == 128 && c == 64) return gram_t<128, 64>(p, s);
+  if (d == 96 && c == 128) return gram_t<96, 128>(p, s);
+  if (d == 96 && c == 64) return gram_t<96, 64>(p, s);
+  if (d == 64 && c == 128) return gram_t<64, 128>(p, s);
+  if (d == 64 && c == 64) return gram_t<64, 64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+template <int D, int C>
+static hipError_t power_t(const PddpParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((pddp_gram_power_kernel<D, C>), dim3((unsigned)(p.bh * ((int64_t)1 << p.level))), dim3(256),
+                     0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_pddp_gram_power(int d, int c, const PddpParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.bh * ((int64_t)1 << p.level)));
-  if (d == 128 && c == 128) hipLaunchKernelGGL((pddp_gram_power_kernel<128, 128>), grid, dim3(256), 0, s, p);
-  else if (d == 128 && c == 64) hipLaunchKernelGGL((pddp_gram_power_kernel<128, 64>), grid, dim3(256), 0, s, p);
-  else if (d == 64 && c == 128) hipLaunchKernelGGL((pddp_gram_power_kernel<64, 128>), grid, dim3(256), 0, s, p);
-  else if (d == 64 && c == 64) hipLaunchKernelGGL((pddp_gram_power_kernel<64, 64>), grid, dim3(256), 0, s, p);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (d == 128 && c == 128) return power_t<128, 128>(p, s);
+  if (d == 128 && c == 64) return power_t<128, 64>(p, s);
+  if (d == 96 && c == 128) return power_t<96, 128>(p, s);
+  if (d == 96 && c == 64) return power_t<96, 64>(p, s);
+  if (d == 64 && c == 128) return power_t<64, 128>(p, s);
+  if (d == 64 && c == 64) return power_t<64, 64>(p, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_pddp_split(int c, const PddpParams& p, hipStream_t s) {

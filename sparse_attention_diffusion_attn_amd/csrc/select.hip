@@ -336,6 +336,8 @@ static hipError_t launch_scores_t(const ScoreParams& p, hipStream_t s) {
 hipError_t launch_scores(int d, int c, const ScoreParams& p, hipStream_t s) {
   if (d == 128 && c == 128) return launch_scores_t<128, 128>(p, s);
   if (d == 128 && c == 64) return launch_scores_t<128, 64>(p, s);
+  if (d == 96 && c == 128) return launch_scores_t<96, 128>(p, s);
+  if (d == 96 && c == 64) return launch_scores_t<96, 64>(p, s);
   if (d == 64 && c == 128) return launch_scores_t<64, 128>(p, s);
   if (d == 64 && c == 64) return launch_scores_t<64, 64>(p, s);
   return hipErrorInvalidValue;

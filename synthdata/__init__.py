@@ -92,6 +92,8 @@ CONFIGS = {
     "hunyuan720p_25": LayerConfig("hunyuan720p_25", 1, 24, 118800, 128, 128, 25, 128, 0.3, 8, 0.05,
                                   grid=(33, 45, 80)),
     "3d": LayerConfig("3d", 1, 16, 65536, 64, 128, 15, 256, 0.2, 10, 0.03, grid=(1, 256, 256)),
+    # the 480p layer with 96-dimensional heads (another head size of DiT stacks)
+    "480p_d96": LayerConfig("480p_d96", 1, 24, 32760, 96, 128, 25, 64, 0.3, 4, 0.05, grid=(13, 42, 60)),
 }
 
 

@@ -42,7 +42,7 @@ int main(void) {
                        NULL, fake + 128, NULL);
   CHECK(st == MCS_ERR_INVALID_ARG);
   CHECK(strstr(mcs_last_error(), "q is NULL") != NULL);
-  d.head_dim = 96;
+  d.head_dim = 80;
   st = mcs_dense_attn(&d, fake, fake, fake, 0.1f, fake + 128, NULL, NULL);
   CHECK(st == MCS_ERR_UNSUPPORTED);
   d.head_dim = 128;

@@ -51,11 +51,13 @@ def test_workspace_sizes():
     assert lib.mcs_anchor_select_min_workspace_bytes(ctypes.byref(dm), 250) == per_head
     assert lib.mcs_anchor_select_workspace_bytes(ctypes.byref(dm), 250) == 2 * per_head
     assert lib.mcs_anchor_select_workspace_bytes(ctypes.byref(dm), 0) == 0
-    assert lib.mcs_group_workspace_bytes(ctypes.byref(d(head_dim=96))) == 0
+    assert lib.mcs_group_workspace_bytes(ctypes.byref(d(head_dim=80))) == 0
+    assert lib.mcs_group_workspace_bytes(ctypes.byref(d(head_dim=96))) > 0
 
 
 @pytest.mark.parametrize("kw,code,msg", [
-    (dict(head_dim=96), mcs.MCS_ERR_UNSUPPORTED, "head_dim"),
+    (dict(head_dim=80), mcs.MCS_ERR_UNSUPPORTED, "head_dim"),
+    (dict(head_dim=256), mcs.MCS_ERR_UNSUPPORTED, "head_dim"),
     (dict(group_size=32), mcs.MCS_ERR_UNSUPPORTED, "group_size"),
     (dict(n_pad=1000, n_valid=900), mcs.MCS_ERR_INVALID_ARG, "multiple"),
     (dict(n_valid=0), mcs.MCS_ERR_INVALID_ARG, "n_valid"),
@@ -295,3 +297,18 @@ def test_noalloc_validation_before_any_gpu_work():
     assert lib.mcs_anchor_select_noalloc(ctypes.byref(d()), P, P, P, P, 0, 0.1, P, P, P, None) == \
         mcs.MCS_ERR_INVALID_ARG
     assert "topk" in err()
+
+
+def test_head_dim_96_scope():
+    """d = 96 runs through the five calls of the method; the k-means
+    comparator and the block-selection variants stay at d = 64 and 128."""
+    lib = mcs.lib()
+    d96 = d(head_dim=96)
+    assert lib.mcs_anchor_select_workspace_bytes(ctypes.byref(d96), 250) > 0
+    assert lib.mcs_group_kmeans_workspace_bytes(ctypes.byref(d96)) == 0
+    assert lib.mcs_group_kmeans(ctypes.byref(d96), P, 3, P, None, P, 1 << 30, None) == mcs.MCS_ERR_UNSUPPORTED
+    assert "k-means" in err()
+    assert lib.mcs_block_select_workspace_bytes(ctypes.byref(d96), mcs.BLOCK_EXACT, 64, 4) == 0
+    assert lib.mcs_block_select(ctypes.byref(d96), P, P, P, P, mcs.BLOCK_EXACT, 64, 4, 0.1, P, P, P,
+                                1 << 30, None) == mcs.MCS_ERR_UNSUPPORTED
+    assert "block selection" in err()

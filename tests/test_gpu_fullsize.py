@@ -45,7 +45,7 @@ def data_for(cfg):
                       cfg.drift, cfg.seed)
 
 
-FULL = ["480p", "3d", "wan720p", "hunyuan720p_15", "hunyuan720p_25", "480p_c64"]
+FULL = ["480p", "3d", "wan720p", "hunyuan720p_15", "hunyuan720p_25", "480p_c64", "480p_d96"]
 # the 480p layer with groups of 64 queries (the split-key-tile attention path)
 EXTRA = {"480p_c64": sd.custom("480p_c64", heads=24, n_valid=32760, head_dim=128, group_size=64,
                                density_pct=25, n_clusters=64)}
@@ -129,7 +129,7 @@ def test_fullsize_pipeline_sampled(mcs, name):
           f"max err / bound {worst_frac:.3f}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["480p", "3d", "hunyuan720p_15"])
+@pytest.mark.parametrize("name", ["480p", "3d", "hunyuan720p_15", "480p_d96"])
 def test_fullsize_group_levels(mcs, name):
     cfg = sd.CONFIGS[name]
     (q, _, _), _ = data_for(cfg)

@@ -45,6 +45,8 @@ SHAPES = [  # (d, C, n_valid, n_pad, topk, heads)
     (128, 128, 500, 512, 77, 2),
     (128, 64, 700, 704, 129, 1),
     (64, 128, 1024, 1024, 1024, 1),
+    (96, 128, 700, 768, 150, 2),
+    (96, 64, 900, 960, 201, 1),
     (128, 128, 384, 384, 1, 1),
     (128, 128, 300, 384, 64, 1),
 ]
@@ -84,7 +86,7 @@ def test_sparse_attn_random_metadata(mcs, shape):
             par.assert_close(f64(o_nr[0, h])[:nv], ref_nr[:nv], what=f"sparse head {h}")
 
 
-@pytest.mark.parametrize("shape", SHAPES[:4], ids=lambda s: "d%d_C%d_n%d_%d_k%d_h%d" % s)
+@pytest.mark.parametrize("shape", SHAPES[:6], ids=lambda s: "d%d_C%d_n%d_%d_k%d_h%d" % s)
 def test_dense_attn(mcs, shape):
     d, C, nv, n_pad, topk, H = shape
     cfg = sd.custom(heads=H, n_valid=nv, head_dim=d, group_size=C, n_clusters=8, n_reuse=0)
@@ -121,6 +123,8 @@ TINY_LIKE = [
     sd.custom("ragged128", heads=2, n_valid=700, head_dim=128, group_size=128, density_pct=25, n_clusters=8),
     sd.custom("ragged64", heads=1, n_valid=900, head_dim=64, group_size=128, density_pct=15, n_clusters=12),
     sd.custom("c64d128", heads=1, n_valid=1500, head_dim=128, group_size=64, density_pct=20, n_clusters=10),
+    sd.custom("d96", heads=2, n_valid=1000, head_dim=96, group_size=128, density_pct=20, n_clusters=10),
+    sd.custom("d96c64", heads=1, n_valid=1300, head_dim=96, group_size=64, density_pct=25, n_clusters=12),
 ]
 
 
@@ -192,6 +196,27 @@ def test_group_level_by_level(mcs, cfg):
             swaps += par.check_split_level(f64(q[0, h]), perms[lv][h], perms[lv + 1][h], cfg.group_size,
                                            cfg.groups, lv, cfg.power_iters)
     print(f"{cfg.name}: {swaps} band swaps")
+
+
+@pytest.mark.parametrize("iters", [0, 1, 3])
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_group_few_power_iterations(mcs, d, iters):
+    """Grouping with 0 (projections on v0 = 1/sqrt(d), node means from the
+    row-sum pass), 1 and 3 power iterations, level by level against the
+    oracle's splits with the same iteration count."""
+    cfg = sd.custom(f"it{iters}d{d}", heads=2, n_valid=900, head_dim=d, group_size=64, n_clusters=7)
+    q = sd.generate(cfg, steps=1)[0][0]
+    qd = q.to(DEV)
+    L = cfg.levels
+    perms = [np.tile(np.arange(cfg.n_pad), (cfg.heads, 1))]
+    for lv in range(1, L + 1):
+        perms.append(mcs.group(qd, cfg.n_valid, cfg.group_size, iters, max_levels=lv)[0].cpu().numpy())
+    swaps = 0
+    for h in range(cfg.heads):
+        for lv in range(L):
+            swaps += par.check_split_level(f64(q[0, h]), perms[lv][h], perms[lv + 1][h], cfg.group_size,
+                                           cfg.groups, lv, iters)
+    print(f"{iters} iterations, d {d}: {swaps} band swaps")
 
 
 def test_determinism(mcs):
