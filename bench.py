@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--config", default="hunyuan720p_25")
     ap.add_argument("--also-density", type=int, default=None,
                     help="second density (percent) measured on the same inputs "
-                         "(default: 15 for the 25%% Hunyuan layer, none otherwise)")
+                         "(default: 15 for the 25%% Hunyuan layer, none otherwise; 0 = none)")
     ap.add_argument("--reuse-inputs", type=int, default=2,
                     help="distinct drifted reuse-step inputs the reuse steps cycle over")
     ap.add_argument("--ratio-reps", type=int, default=10, help="reps of the dense-vs-sparse timing")
@@ -292,7 +292,7 @@ def main():
     # the same layer at a second density: a second selection on the same
     # inputs and groups, its residual, its reuse-step sparse attention
     second = None
-    if also is not None:
+    if also:
         k2 = (nv * also + 99) // 100
         kv2 = torch.empty((B, H, G, k2), dtype=torch.int32, device=dev)
         r2 = torch.empty_like(q0)
