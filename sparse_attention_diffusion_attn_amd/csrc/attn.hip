@@ -20,8 +20,17 @@
 // so every lane owns one query row for the whole online softmax (fp32, exp2
 // with the scale folded in); the only cross-lane step is one max exchange
 // between the two 32-lane halves, done in the VALU.
+// Softmax does not depend on the offset subtracted from the logits, so the
+// first pass uses none: p = exp2(s * scale * log2 e) straight from the
+// accumulators, with no row max at all.  That is exact while every row's
+// probability sum stays inside [2^-60, 2^64] and O is finite; a row outside
+// (logits beyond about +-60 in log2 units) makes the workgroup redo the group
+// with the lazily raised running max, which a dense call that returns the
+// log-sum-exp always uses.
 // The dense mode runs the very same code with contiguous key rows, so the
 // sparse/dense time ratio measures the cost of gathering alone.
+#include <type_traits>
+
 #include "mcs_common.h"
 #include "mcs_internal.h"
 
@@ -29,6 +38,12 @@ namespace mcs {
 
 // Headroom of the lazily updated running max, in log2 units.
 constexpr float kLazyLog2 = 8.0f;
+// Row sums the zero-offset pass accepts: up to 2^64, probabilities keep full
+// fp32 / bf16 relative precision and O stays far from overflow; from 2^-60 up,
+// the largest probability of a row of up to 2^24 keys is at least 2^-84, so
+// any that underflow (below 2^-126) weigh less than 2^-42 of the row.
+constexpr float kZeroOffMaxSum = 18446744073709551616.0f;  // 2^64
+constexpr float kZeroOffMinSum = 8.673617379884035e-19f;   // 2^-60
 __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <int D, int C, int MODE>
@@ -153,24 +168,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const int voff_b = (vrow + 8) * 64 + ((vchunk ^ h ^ 2) << 4) + vhalf;
 
   f32x16 o[NPL];
-#pragma unroll
-  for (int T = 0; T < NPL; ++T)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) o[T][j] = 0.f;
-  float mrun = -INFINITY, lrun = 0.f;
+  float mrun, lrun;
   const float c2 = p.scale * kLog2e;
-
-  fetch_idx(0);
-  issue(0);
-  if (ntiles > 1) fetch_idx(1);
+  __shared__ int redo;
+  if (threadIdx.x == 0) redo = 0;
 
   // One key tile: the copies of tile t+1 go to kdst_n (the other buffer)
   // while kbuf/vbuf (this tile's K and V) are read.  The three pointers are
   // restrict-qualified: the compiler then knows that the LDS reads cannot
   // alias the copies in flight, and does not make the transposing V reads
   // wait for those copies (it would otherwise insert a vmcnt(0) before them).
-  auto tile = [&](int t, char* __restrict__ kdst_n, const char* __restrict__ kbuf,
+  auto tile = [&](auto fixed, int t, char* __restrict__ kdst_n, const char* __restrict__ kbuf,
                   const char* __restrict__ vbuf) __attribute__((always_inline)) {
+    constexpr bool FIXED = decltype(fixed)::value;
     const bool more = t + 1 < ntiles;
 
     // S^T = K . Q^T for the 64 keys of this tile (two 32-key blocks).  The K
@@ -241,29 +251,32 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     // the other half of the tile's keys).  The running max is only raised when
     // the tile's max exceeds it by more than kLazyLog2 (in log2 units), so the
     // rescale of O and l is skipped on almost every tile; probabilities stay
-    // below 2^kLazyLog2 and the final O / l is unchanged.
-    float mx = s0[0];
+    // below 2^kLazyLog2 and the final O / l is unchanged.  The zero-offset
+    // pass skips it (mrun stays 0).
+    if constexpr (!FIXED) {
+      float mx = s0[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s0[j]);
-    if (!SPLIT) {
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s0[j]);
+      if (!SPLIT) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s1[j]);
-    }
-    mx = max_xor32(mx);
-    const bool raise = (mx - mrun) * c2 > kLazyLog2;
-    if (__any(raise)) {
-      const float mnew = raise ? mx : mrun;
-      const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c2);
-      mrun = mnew;
-      lrun *= alpha;
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s1[j]);
+      }
+      mx = max_xor32(mx);
+      const bool raise = (mx - mrun) * c2 > kLazyLog2;
+      if (__any(raise)) {
+        const float mnew = raise ? mx : mrun;
+        const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c2);
+        mrun = mnew;
+        lrun *= alpha;
 #pragma unroll
-      for (int T = 0; T < NPL; ++T)
+        for (int T = 0; T < NPL; ++T)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[T][j] *= alpha;
+          for (int j = 0; j < 16; ++j) o[T][j] *= alpha;
+      }
     }
     // (SPLIT: a half that has seen no valid key yet keeps mrun = -inf; its
     // probabilities are then exp2(-inf) = 0 rather than NaN)
-    const float mc = (SPLIT && mrun == -INFINITY) ? 0.f : mrun * c2;
+    const float mc = (FIXED || (SPLIT && mrun == -INFINITY)) ? 0.f : mrun * c2;
     bf16x8 pb[NU];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -303,45 +316,88 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     }
   };
 
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vm0();
-    __syncthreads();
-    tile(t, lds + ((t + 1) & 1) * 2 * TILE + w * IPW * 1024, lds + (t & 1) * 2 * TILE,
-         lds + (t & 1) * 2 * TILE + TILE);
-  }
-
-  // ---- epilogue ----
-  float lsum = sum_xor32(lrun);
-  if constexpr (SPLIT) {
-    // merge the two key halves of each row block: the kh = 1 wavefront hands
-    // its running max, row sum and O to the kh = 0 one through LDS (the tile
-    // buffers are free once every wavefront has passed the barrier; no copy is
-    // in flight after the last tile), and the kh = 0 wavefront rescales both
-    // to the common max
-    constexpr int NV = NPL * 16 + 2;    // values per lane
-    float* xo = reinterpret_cast<float*>(lds) + rb * NV * 64 + lane;
-    __syncthreads();
-    if (kh == 1) {
-#pragma unroll
-      for (int T = 0; T < NPL; ++T)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) xo[(T * 16 + j) * 64] = o[T][j];
-      xo[(NPL * 16) * 64] = mrun;
-      xo[(NPL * 16 + 1) * 64] = lsum;
-    }
-    __syncthreads();
-    if (kh == 1) return;                // no barrier follows
-    const float m1 = xo[(NPL * 16) * 64], l1 = xo[(NPL * 16 + 1) * 64];
-    const float m = fmaxf(mrun, m1);    // mrun is finite: key 0 lies in half 0
-    const float f0 = __builtin_amdgcn_exp2f((mrun - m) * c2);
-    const float f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c2);
+  auto run = [&](auto fixed) {
+    constexpr bool FIXED = decltype(fixed)::value;
 #pragma unroll
     for (int T = 0; T < NPL; ++T)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) o[T][j] = o[T][j] * f0 + xo[(T * 16 + j) * 64] * f1;
-    lsum = lsum * f0 + l1 * f1;
-    mrun = m;
+      for (int j = 0; j < 16; ++j) o[T][j] = 0.f;
+    mrun = FIXED ? 0.f : -INFINITY;
+    lrun = 0.f;
+    fetch_idx(0);
+    issue(0);
+    if (ntiles > 1) fetch_idx(1);
+    for (int t = 0; t < ntiles; ++t) {
+      wait_vm0();
+      __syncthreads();
+      tile(fixed, t, lds + ((t + 1) & 1) * 2 * TILE + w * IPW * 1024, lds + (t & 1) * 2 * TILE,
+           lds + (t & 1) * 2 * TILE + TILE);
+    }
+  };
+
+  // Row sum over the lane pair; with C = 64 the two key halves of each row
+  // block are merged here: the kh = 1 wavefront hands its running max, row sum
+  // and O to the kh = 0 one through LDS (the tile buffers are free once every
+  // wavefront has passed the barrier; no copy is in flight after the last
+  // tile), and the kh = 0 wavefront rescales both to the common max.
+  auto finish = [&]() -> float {
+    float lsum = sum_xor32(lrun);
+    if constexpr (SPLIT) {
+      constexpr int NV = NPL * 16 + 2;    // values per lane
+      float* xo = reinterpret_cast<float*>(lds) + rb * NV * 64 + lane;
+      __syncthreads();
+      if (kh == 1) {
+#pragma unroll
+        for (int T = 0; T < NPL; ++T)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) xo[(T * 16 + j) * 64] = o[T][j];
+        xo[(NPL * 16) * 64] = mrun;
+        xo[(NPL * 16 + 1) * 64] = lsum;
+      }
+      __syncthreads();
+      if (kh == 0) {
+        const float m1 = xo[(NPL * 16) * 64], l1 = xo[(NPL * 16 + 1) * 64];
+        const float m = fmaxf(mrun, m1);  // mrun is finite: key 0 lies in half 0
+        const float f0 = __builtin_amdgcn_exp2f((mrun - m) * c2);
+        const float f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c2);
+#pragma unroll
+        for (int T = 0; T < NPL; ++T)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[T][j] = o[T][j] * f0 + xo[(T * 16 + j) * 64] * f1;
+        lsum = lsum * f0 + l1 * f1;
+        mrun = m;
+      }
+    }
+    return lsum;
+  };
+
+  // The row sums add the bf16-rounded probabilities, so a row's largest term
+  // is exact only when the offset is the row max (it is then exp2(0) = 1).  A
+  // log-sum-exp output (the anchor's dense pass, whose lse weighs every key of
+  // the score pass) therefore always takes the running-max pass.
+  float lsum;
+  bool zero_pass = !(MODE == ATTN_DENSE && p.lse != nullptr);
+  if (zero_pass) {
+    run(std::true_type{});
+    lsum = finish();
+    // range check on the (merged) rows; any failing row redoes the whole group
+    bool ok = lsum >= kZeroOffMinSum && lsum <= kZeroOffMaxSum;
+#pragma unroll
+    for (int T = 0; T < NPL; ++T)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ok = ok && __builtin_isfinite(o[T][j]);
+    if (SPLIT && kh == 1) ok = true;    // its values live in the kh = 0 wavefront now
+    if (__any(!ok) && lane == 0) redo = 1;
+    __syncthreads();
+    zero_pass = (redo == 0);
   }
+  if (!zero_pass) {
+    run(std::false_type{});
+    lsum = finish();
+  }
+  if (SPLIT && kh == 1) return;         // no barrier follows
+
+  // ---- epilogue ----
   const float inv = 1.f / lsum;
   const bool valid = qrow < p.n_valid;
   uint16_t* Ob = p.out + head_offset(p.so, bh, p.heads) + (int64_t)qrow * p.so.n;

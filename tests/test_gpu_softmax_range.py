@@ -1,13 +1,21 @@
-"""Attention on logits with a large, rising range: the lazily raised running max.
+"""Attention on logits of a large range: both softmax passes.
 
-The kernels keep a running row max that is raised only when a tile's max
-exceeds it by more than 8 in log2 units; only then are O and the row sum
-rescaled.  Clustered synthetic data hardly ever triggers that.  Here the keys
-grow along one direction u, key j as (j/64)·u plus noise, so for a query near
-+u each 64-key tile's max beats the last by 11 to 16 log2 units and every
-tile rescales.  For a query near -u the first tile holds the max and no tile
-rescales.  Even and odd rows alternate between the two, so the lanes of every
-wavefront disagree on whether to raise.  Logits reach 140 to 190 in log2 units.
+The attention kernel first runs with no offset at all (p = exp2 of the scaled
+logit, no row max) and accepts that pass when every row's probability sum
+stays in [2^-60, 2^64] and O is finite; otherwise the workgroup redoes the
+group with a running row max that is raised only when a tile's max exceeds it
+by more than 8 in log2 units.  Clustered synthetic data stays in the first
+pass.  Here the keys grow along one direction u, key j as (slope·j/64)·u plus
+noise, so for a query near +u each 64-key tile's max beats the last by a fixed
+step; for a query near -u the first tile holds the max; even and odd rows
+alternate between the two.
+- "rising" (slope 1): steps of 11 to 16 log2 units, logits reach 140 to 190,
+  the first pass overflows its range and the redo raises the running max on
+  every tile.
+- "gentle" (slope 1/4): steps of 3 to 4 units, logits stay below about 50, and
+  the first pass is accepted with probabilities up to about 2^48.
+- "negative": every logit below -80 in log2 units, so the first pass
+  underflows its range and the redo takes over from below.
 Dense attention (O and the log-sum-exp), the anchor's score pass and top-k,
 the reuse step and the residual are checked against the fp64 oracle on the
 same bf16 inputs.
@@ -32,10 +40,10 @@ def mcs():
     return m
 
 
-def rising_inputs(d, n_valid, n_pad, seed):
+def rising_inputs(d, n_valid, n_pad, seed, slope=1.0):
     rng = np.random.default_rng(seed)
     u = rng.choice([-1.0, 1.0], size=d)
-    ramp = np.arange(n_pad) / 64.0
+    ramp = slope * np.arange(n_pad) / 64.0
     k = ramp[:, None] * u[None, :] + 0.5 * rng.standard_normal((n_pad, d))
     sign = np.where(np.arange(n_pad) % 2 == 0, 1.0, -1.0)
     q = sign[:, None] * u[None, :] + 0.3 * rng.standard_normal((n_pad, d))
@@ -47,11 +55,31 @@ def rising_inputs(d, n_valid, n_pad, seed):
     return out
 
 
+def negative_inputs(d, n_valid, n_pad, seed):
+    """Every logit far below -60 in log2 units (about -110, a spread of about 1
+    across the keys of a row, so attention is diffuse)."""
+    rng = np.random.default_rng(seed)
+    u = rng.choice([-1.0, 1.0], size=d)
+    beta = 110.0 / (np.sqrt(d) * np.log2(np.e))
+    k = u[None, :] + 0.1 * rng.standard_normal((n_pad, d))
+    q = -beta * u[None, :] + 0.3 * rng.standard_normal((n_pad, d))
+    v = rng.standard_normal((n_pad, d))
+    out = []
+    for x in (q, k, v):
+        x[n_valid:] = 0.0
+        out.append(torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).reshape(1, 1, n_pad, d))
+    return out
+
+
+@pytest.mark.parametrize("case", ["rising", "gentle", "negative"])
 @pytest.mark.parametrize("d,C", [(128, 128), (64, 64)])
-def test_rising_logits_dense_sparse_residual(mcs, d, C):
+def test_logit_range_dense_sparse_residual(mcs, d, C, case):
     n_valid, n_pad = 700, 768            # 11 key tiles, the last one ragged (60 keys)
-    print(f"rising logits d{d} C{C}", flush=True)
-    q, k, v = rising_inputs(d, n_valid, n_pad, seed=d + C)
+    print(f"logit range {case} d{d} C{C}", flush=True)
+    if case == "negative":
+        q, k, v = negative_inputs(d, n_valid, n_pad, seed=d + C)
+    else:
+        q, k, v = rising_inputs(d, n_valid, n_pad, seed=d + C, slope=1.0 if case == "rising" else 0.25)
     sc = 1.0 / np.sqrt(d)
     qf, kf, vf = (par.bf16_to_f64(t[0, 0]) for t in (q, k, v))
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
@@ -60,8 +88,15 @@ def test_rising_logits_dense_sparse_residual(mcs, d, C):
     o, lse = mcs.dense_attn(qd, kd, vd, n_valid, C, sc)
     torch.cuda.synchronize()
     ref_o, ref_l = orc.dense_attention(qf, kf, vf, n_valid, sc)
-    s_max = float(np.max(qf[:n_valid] @ kf[:n_valid].T)) * sc * np.log2(np.e)
-    assert s_max > 120.0, "the inputs do not reach the intended logit range"
+    logits = (qf[:n_valid] @ kf[:n_valid].T) * sc * np.log2(np.e)
+    s_max = float(logits.max())
+    if case == "rising":
+        assert s_max > 120.0, "the inputs do not reach the intended logit range"
+    elif case == "gentle":
+        # every row's sum stays inside the zero-offset pass's [2^-60, 2^64]
+        assert 25.0 < s_max < 55.0 and float(logits.max(axis=1).min()) > -50.0, "logits outside the intended range"
+    else:
+        assert s_max < -70.0, "the inputs do not reach the intended logit range"
     par.assert_close(par.bf16_to_f64(o[0, 0].cpu())[:n_valid], ref_o[:n_valid], what="dense O")
     got_l = lse[0, 0].double().cpu().numpy()[:n_valid]
     assert np.abs(got_l - ref_l[:n_valid]).max() <= 1e-4 * np.abs(ref_l[:n_valid]).max()
