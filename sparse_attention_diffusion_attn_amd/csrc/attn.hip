@@ -18,8 +18,8 @@
 //   O^T += V_tile^T . P^T (A = V via transposing LDS reads, B = P from the S^T
 //                          accumulators, converted to bf16)
 // so every lane owns one query row for the whole online softmax (fp32, exp2
-// with the scale folded in); the only cross-lane step is one max exchange
-// between the two 32-lane halves, done in the VALU.
+// with the scale folded in); the only cross-lane step, in the running-max
+// pass, is one max exchange between the two 32-lane halves, done in the VALU.
 // Softmax does not depend on the offset subtracted from the logits, so the
 // first pass uses none: p = exp2(s * scale * log2 e) straight from the
 // accumulators, with no row max at all.  That is exact while every row's
@@ -41,7 +41,8 @@ constexpr float kLazyLog2 = 8.0f;
 // Row sums the zero-offset pass accepts: up to 2^64, probabilities keep full
 // fp32 / bf16 relative precision and O stays far from overflow; from 2^-60 up,
 // the largest probability of a row of up to 2^24 keys is at least 2^-84, so
-// any that underflow (below 2^-126) weigh less than 2^-42 of the row.
+// the ones that underflow (each below 2^-126) weigh less than 2^-18 of the
+// row all together.
 constexpr float kZeroOffMaxSum = 18446744073709551616.0f;  // 2^64
 constexpr float kZeroOffMinSum = 8.673617379884035e-19f;   // 2^-60
 __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
