@@ -58,10 +58,16 @@ def parse():
 
 
 def source_hash(*names):
+    """Hash of the kernel sources' code: // comments and blank lines are
+    dropped and whitespace collapsed, so that a comment edit does not
+    invalidate a measurement taken on the same code."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "sparse_attention_diffusion_attn_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_attention_diffusion_attn_amd", "csrc", n)) as f:
+            for line in f:
+                code = " ".join(line.split("//", 1)[0].split())
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
