@@ -128,3 +128,44 @@ def test_logit_range_dense_sparse_residual(mcs, d, C, case):
     kv_h = kv_a[0, 0].cpu().numpy()
     for g in range(G):
         par.check_selection(kv_h[g], a[g], topk)
+
+
+@pytest.mark.parametrize("d,C", [(128, 128), (64, 64)])
+def test_redo_in_some_groups_of_one_launch(mcs, d, C):
+    """One reuse-step launch in which some groups take the redo and the others
+    keep the first pass: with the rising inputs, rows near +u overflow the
+    first pass's range and rows near -u do not; a perm that lists the +u rows
+    first gives groups of only +u rows, one mixed group, and groups of only -u
+    rows.  Both kinds are checked against the oracle in the same launch."""
+    n_valid, n_pad = 700, 768
+    print(f"redo in some groups d{d} C{C}", flush=True)
+    q, k, v = rising_inputs(d, n_valid, n_pad, seed=3 * d + C)
+    sc = 1.0 / np.sqrt(d)
+    qf, kf, vf = (par.bf16_to_f64(t[0, 0]) for t in (q, k, v))
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    G, topk = n_pad // C, 333
+    rows = np.arange(n_valid)
+    perm = np.concatenate([rows[rows % 2 == 0], rows[rows % 2 == 1], np.arange(n_valid, n_pad)]).astype(np.int32)
+    rng = np.random.default_rng(11)
+    kv = np.stack([np.sort(rng.choice(n_valid, topk, replace=False)) for _ in range(G)]).astype(np.int32)
+    # each group's largest row sum of 2^(scaled logit) over its keys, in log2
+    # units: beyond 64 the first pass is rejected, inside [-60, 64] it is kept
+    log2sum = []
+    for g in range(G):
+        members = [int(i) for i in perm[g * C:(g + 1) * C] if i < n_valid]
+        if not members:                  # a group of padding rows only
+            continue
+        lg = (qf[members] @ kf[kv[g]].T) * sc * np.log2(np.e)
+        m = lg.max(axis=1, keepdims=True)
+        log2sum.append(float((m[:, 0] + np.log2(np.exp2(lg - m).sum(axis=1))).max()))
+    redo = [x > 64.0 for x in log2sum]
+    assert any(redo) and not all(redo), f"the launch is not mixed: {log2sum}"
+    assert all(x > -60.0 for x in log2sum)
+    r = torch.from_numpy(0.05 * rng.standard_normal((1, 1, n_pad, d)).astype(np.float32)).to(torch.bfloat16)
+    r[:, :, n_valid:] = 0
+    pd = torch.from_numpy(perm).reshape(1, 1, n_pad).to(DEV)
+    kvd = torch.from_numpy(kv).reshape(1, 1, G, topk).to(DEV)
+    os_ = mcs.sparse_attn(qd, kd, vd, pd, kvd, r.to(DEV), n_valid, C, sc)
+    torch.cuda.synchronize()
+    ref_s = orc.reuse_step(qf, kf, vf, perm, kv, par.bf16_to_f64(r[0, 0]), n_valid, C, sc)
+    par.assert_close(par.bf16_to_f64(os_[0, 0].cpu())[:n_valid], ref_s[:n_valid], what="reuse step")
