@@ -131,15 +131,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const __amdgpu_buffer_rsrc_t irs =
       (MODE == ATTN_DENSE) ? krs : make_rsrc(idxrow, (uint32_t)nk * 4u);
   int tok[NTOK];
+  // A lane's keys are 4*(l/4) + ins_key(i).  With four copies per wavefront
+  // (d = 128) they are the four consecutive keys from 4*(l/4), read with one
+  // 16-byte load instead of four 4-byte ones (fewer wavefronts through the
+  // vector-memory path, which the copies keep busy); otherwise one 4-byte
+  // load each.
   auto fetch_idx = [&](int t) {
     const int key0 = t * KT + j4;
+    if (MODE == ATTN_DENSE) {
 #pragma unroll
-    for (int i = 0; i < NTOK; ++i) {
-      if (MODE == ATTN_DENSE) {
-        tok[i] = key0 + ins_key(i);
-      } else {
+      for (int i = 0; i < NTOK; ++i) tok[i] = key0 + ins_key(i);
+    } else if constexpr (IPW == 4) {
+      const i32x4 x = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(irs, (uint32_t)key0 * 4u, 0, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tok[i] = x[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NTOK; ++i)
         tok[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, (uint32_t)(key0 + ins_key(i)) * 4u, 0, 0);
-      }
     }
   };
   auto issue = [&](int buf) {
