@@ -118,8 +118,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   // fixed order of the keys inside a tile is valid, as K and V share it and
   // only the final-tile mask looks at key positions.  K, V and the index row
   // are read through buffer resources with 32-bit offsets (row * row stride,
-  // a 24-bit multiply); reads past a resource's end return zero, which the
-  // final-tile mask covers for the index row.
+  // a 24-bit multiply); reads past a resource's end return zero (dword by
+  // dword, so a 16-byte index load that straddles the end still returns its
+  // valid entries), which the final-tile mask covers for the index row.
   constexpr int NTOK = IPW < 4 ? IPW : 4;     // distinct keys per lane per tile
   auto ins_key = [&](int i) { return (w * IPW + i) & 3; };                  // key offset of copy i
   auto ins_plane = [&](int i) { return (uint32_t)((w * IPW + i) >> 2) * 64u; };  // its plane's byte offset
